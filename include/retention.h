@@ -1,0 +1,158 @@
+/*
+ * retention.h -- C ABI of the MI355X (gfx950) multi-scale retention library.
+ *
+ * What is computed (pages cited by title and section):
+ *   "Retentive Network: A Successor to Transformer for Large Language Models",
+ *   paper summary on blog.csdn.net:
+ *     Sec. 2.1 "Retention": scalar-gamma retention
+ *         o_n = sum_{m<=n} gamma^(n-m) (Q_n e^{i n theta}) (K_m e^{i m theta})^dagger v_m
+ *       and its three representations -- (1) parallel (Q K^T (.) D) V with
+ *       D_nm = gamma^(n-m) for n >= m else 0; (2) recurrent
+ *       S_n = gamma S_{n-1} + K_n^T V_n, o_n = Q_n S_n; (3) chunkwise recurrent
+ *       (parallel inside a chunk, recurrent across chunks).
+ *     Sec. 2.2 "Gated Multi-Scale Retention": per-head gamma, per-head
+ *       GroupNorm, MSR(X) = (swish(X W_G) (.) Y) W_O.
+ *   "RetNet dual-mode hands-on manual" (lanjinlin.com.cn), Sec. 1 (decay
+ *     matrix), Sec. 3.2 (explicit per-sequence state for recurrent inference),
+ *     Sec. 4.1 (mode switch with states passed in and out).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates or frees tensor memory and keeps no pointer
+ *     after a call returns.  Tensors are dense row-major in the shapes given,
+ *     16-byte aligned.
+ *   - Positions are 0-based.  Token n of a call is at absolute position
+ *     p = pos0 + n.
+ *   - Rotation (xPOS phase): coordinates (2i, 2i+1) of a q or k row form the
+ *     complex number x_{2i} + i x_{2i+1}, multiplied by exp(i p theta_i).  The
+ *     score of query n and key m is the real dot product of the rotated rows,
+ *     i.e. Re[q_rot conj(k_rot)].  theta == NULL means no rotation; otherwise
+ *     theta is a HOST array of dk/2 fp32 frequencies and dk must be even.
+ *   - gamma is a HOST array of H fp32 decay constants in [0, 1].  gamma and
+ *     theta are copied into kernel arguments at launch.
+ *   - No 1/sqrt(dk) scaling is applied: scale Q or K beforehand if wanted.
+ *   - gn_eps < 0: no normalisation.  gn_eps >= 0: every output row of dv
+ *     values (one token, one head) is replaced by (o - mean) / sqrt(var + eps),
+ *     biased variance, no affine parameters.
+ *   - Accumulation is fp32.  The recurrent state is fp32 [B,H,dk,dv] and holds
+ *     sum_m gamma^(n-m) k_rot_m^T v_m with keys rotated at their absolute
+ *     positions.
+ *   - All calls are asynchronous on hip_stream (NULL = default stream); none
+ *     synchronises the device.
+ *
+ * Errors: every argument is checked on the host before anything is enqueued.
+ * On any error nothing is enqueued and outputs are untouched.  The library
+ * never aborts, throws or prints.  retention_last_error() gives a message for
+ * the calling thread's last failure.  Asynchronous device faults surface at
+ * the caller's next synchronisation.
+ */
+#ifndef RETENTION_H_
+#define RETENTION_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RETENTION_ABI_VERSION 1
+
+typedef enum {
+  RET_OK = 0,
+  RET_ERR_INVALID_ARG = 1, /* null pointer, bad size, gamma outside [0,1], bad eps, misaligned ... */
+  RET_ERR_UNSUPPORTED = 2, /* legal arguments this build does not handle (see each call) */
+  RET_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_bytes query */
+  RET_ERR_HIP = 4          /* a HIP launch error (hipGetLastError) */
+} ret_status_t;
+
+typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
+
+/* Library limits (UNSUPPORTED beyond them). */
+#define RETENTION_MAX_HEADS 128
+#define RETENTION_MAX_DK 512
+#define RETENTION_MAX_DV 1024
+
+int retention_abi_version(void);
+const char *retention_status_string(int status);
+/* Message describing the calling thread's most recent failed call ("" if none). */
+const char *retention_last_error(void);
+
+/*
+ * Parallel representation (Sec. 2.1 (1)): O = (Q_rot K_rot^T (.) D) V per (b, h),
+ * D_nm = gamma_h^(n-m) for n >= m, else 0; then the optional GroupNorm.
+ *   q, k : [B,H,L,dk] in_dtype          v : [B,H,L,dv] in_dtype
+ *   o    : [B,H,L,dv] out_dtype (must not alias an input)
+ * bf16 inputs with (dk, dv) in {(64,64),(64,128),(128,128),(128,256),(256,256),
+ * (256,512)} use the MFMA kernels; every other case uses the vector (FMA) kernels.
+ * L == 0 is a no-op.
+ */
+ret_status_t retention_parallel(const void *q, const void *k, const void *v, void *o, int B,
+                                int H, int L, int dk, int dv, const float *gamma,
+                                const float *theta, long long pos0, float gn_eps,
+                                ret_dtype_t in_dtype, ret_dtype_t out_dtype, void *hip_stream);
+
+/*
+ * Chunkwise recurrent representation (Sec. 2.1 (3)): tokens are split into
+ * chunks of `chunk` (the last may be shorter).  Inside a chunk the parallel
+ * form is used; the state entering chunk c, S_c, adds gamma^(j+1) q_rot S_c to
+ * token j of the chunk, and S_{c+1} = gamma^Cc S_c + sum_i gamma^(Cc-1-i) k_rot_i^T v_i.
+ *   q, k, v, o : as retention_parallel
+ *   state_in   : [B,H,dk,dv] fp32 state before token 0, or NULL for zeros
+ *   state_out  : [B,H,dk,dv] fp32 state after token L-1, or NULL; may alias state_in
+ *   workspace  : device scratch of at least retention_chunkwise_workspace_bytes()
+ *                bytes (NULL allowed when that is 0); its contents on entry do
+ *                not matter.  Calls sharing a workspace must not overlap.
+ */
+size_t retention_chunkwise_workspace_bytes(int B, int H, int L, int dk, int dv, int chunk,
+                                           ret_dtype_t in_dtype);
+ret_status_t retention_chunkwise(const void *q, const void *k, const void *v, void *o, int B,
+                                 int H, int L, int dk, int dv, int chunk, const float *gamma,
+                                 const float *theta, long long pos0, const float *state_in,
+                                 float *state_out, float gn_eps, ret_dtype_t in_dtype,
+                                 ret_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream);
+
+/*
+ * One recurrent step (Sec. 2.1 (2); the custom operator for the state update
+ * of "RetNet dual-mode hands-on manual" Sec. 4.2):
+ *   S <- gamma_h S + k_rot^T v   (rank-1 update of the dk x dv state)
+ *   o <- q_rot S                 (then the optional GroupNorm)
+ *   q, k  : [B,H,dk] in_dtype     v : [B,H,dv] in_dtype
+ *   state : [B,H,dk,dv] fp32, read then overwritten in place
+ *   o     : [B,H,dv] out_dtype
+ *   pos   : DEVICE int32 [B], absolute position of this token for each
+ *           sequence (used only for rotation; ignored when theta == NULL, and
+ *           may then be NULL).  The caller advances it.
+ */
+ret_status_t retention_recurrent_step(const void *q, const void *k, const void *v, float *state,
+                                      void *o, int B, int H, int dk, int dv, const float *gamma,
+                                      const float *theta, const int *pos, float gn_eps,
+                                      ret_dtype_t in_dtype, ret_dtype_t out_dtype,
+                                      void *hip_stream);
+
+/*
+ * Gated multi-scale retention layer (Sec. 2.2), bf16 in and out:
+ *   Q = X W_Q, K = X W_K, V = X W_V (head h = column block h of width dk / dv)
+ *   head_h = chunkwise retention of (Q_h, K_h, V_h) with gamma_h, theta, pos0
+ *   Y = GroupNorm per (token, head) with gn_eps (>= 0)
+ *   out = (swish(X W_G) (.) Y) W_O,   swish(x) = x / (1 + exp(-x))
+ * Weights are stored transposed ([out, in], one output column per row):
+ *   x   : [B,L,d_model] bf16         y   : [B,L,d_model] bf16
+ *   w_q, w_k : [H*dk, d_model] bf16   w_v, w_g : [H*dv, d_model] bf16
+ *   w_o : [d_model, H*dv] bf16
+ * UNSUPPORTED unless d_model % 64 == 0 and (dk, dv) is one of the MFMA pairs
+ * listed under retention_parallel.
+ */
+size_t msr_layer_fwd_workspace_bytes(int B, int L, int d_model, int H, int dk, int dv,
+                                     int chunk);
+ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, const void *w_v,
+                           const void *w_g, const void *w_o, void *y, int B, int L, int d_model,
+                           int H, int dk, int dv, int chunk, const float *gamma,
+                           const float *theta, long long pos0, float gn_eps, void *workspace,
+                           size_t workspace_bytes, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RETENTION_H_ */

@@ -1,0 +1,252 @@
+// C ABI entry points: host-side validation, workspace sizing and dispatch.
+// Declarations, argument meanings and error behaviour: include/retention.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "retention.h"
+
+using namespace ret;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ret_status_t fail(ret_status_t s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ret_status_t ok() {
+  g_err[0] = '\0';
+  return RET_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t esize(ret_dtype_t t) { return t == RET_BF16 ? 2 : 4; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Checks shared by the three retention entry points.
+ret_status_t check_common(int B, int H, int L, int dk, int dv, const float *gamma,
+                          const float *theta, long long pos0, float gn_eps, ret_dtype_t in_dtype,
+                          ret_dtype_t out_dtype) {
+  if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0 || L < 0)
+    return fail(RET_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d L=%d dk=%d dv=%d)", B, H, L,
+                dk, dv);
+  if ((in_dtype != RET_F32 && in_dtype != RET_BF16) || (out_dtype != RET_F32 && out_dtype != RET_BF16))
+    return fail(RET_ERR_INVALID_ARG, "unknown dtype");
+  if (!gamma) return fail(RET_ERR_INVALID_ARG, "gamma is NULL");
+  if (H > RETENTION_MAX_HEADS) return fail(RET_ERR_UNSUPPORTED, "H=%d above %d", H, RETENTION_MAX_HEADS);
+  if (dk > RETENTION_MAX_DK || dv > RETENTION_MAX_DV)
+    return fail(RET_ERR_UNSUPPORTED, "dk=%d/dv=%d above %d/%d", dk, dv, RETENTION_MAX_DK, RETENTION_MAX_DV);
+  for (int h = 0; h < H; ++h)
+    if (!(gamma[h] >= 0.0f && gamma[h] <= 1.0f))
+      return fail(RET_ERR_INVALID_ARG, "gamma[%d]=%g outside [0,1]", h, (double)gamma[h]);
+  if (theta) {
+    if (dk % 2) return fail(RET_ERR_INVALID_ARG, "rotation needs an even dk (dk=%d)", dk);
+    for (int i = 0; i < dk / 2; ++i)
+      if (!isfinite(theta[i])) return fail(RET_ERR_INVALID_ARG, "theta[%d] not finite", i);
+  }
+  if (isnan(gn_eps) || (gn_eps >= 0.0f && !isfinite(gn_eps)))
+    return fail(RET_ERR_INVALID_ARG, "gn_eps must be finite (or negative for no GroupNorm)");
+  if (pos0 < 0 || pos0 > (1LL << 52) - (long long)L)
+    return fail(RET_ERR_INVALID_ARG, "pos0=%lld outside [0, 2^52 - L]", pos0);
+  return RET_OK;
+}
+
+RetArgs make_args(const void *q, const void *k, const void *v, void *o, int B, int H, int L, int dk,
+                  int dv, int chunk, const float *gamma, const float *theta, long long pos0,
+                  float gn_eps, ret_dtype_t in_dtype, ret_dtype_t out_dtype) {
+  RetArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.gate = nullptr;
+  a.q_sn = dk;
+  a.q_sh = (long long)L * dk;
+  a.q_sb = (long long)H * L * dk;
+  a.v_sn = dv;
+  a.v_sh = (long long)L * dv;
+  a.v_sb = (long long)H * L * dv;
+  a.o_sn = a.v_sn;
+  a.o_sh = a.v_sh;
+  a.o_sb = a.v_sb;
+  a.pos0 = pos0;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.dk = dk;
+  a.dv = dv;
+  a.chunk = chunk;
+  a.in_bf16 = in_dtype == RET_BF16;
+  a.out_bf16 = out_dtype == RET_BF16;
+  a.use_theta = theta != nullptr;
+  a.use_gn = gn_eps >= 0.0f;
+  a.gn_eps = a.use_gn ? gn_eps : 0.0f;
+  for (int h = 0; h < H; ++h) a.gamma[h] = gamma[h];
+  if (theta)
+    for (int i = 0; i < dk / 2; ++i) a.theta[i] = theta[i];
+  return a;
+}
+
+__global__ void copy_or_zero_kernel(float *dst, const float *src, long long n) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i < n; i += (long long)gridDim.x * blockDim.x) dst[i] = src ? src[i] : 0.0f;
+}
+
+hipError_t copy_or_zero(float *dst, const float *src, long long n, hipStream_t st) {
+  if (dst == src || n == 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dst, src, n);
+  return hipGetLastError();
+}
+
+ret_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  return fail(RET_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+}
+
+bool use_mfma(int dk, int dv, ret_dtype_t in_dtype) {
+  return in_dtype == RET_BF16 && mfma_supported(dk, dv);
+}
+
+size_t vec_chunk_ws(int B, int H, int dk, int dv) { return (size_t)B * H * dk * dv * sizeof(float); }
+
+}  // namespace
+
+extern "C" {
+
+int retention_abi_version(void) { return RETENTION_ABI_VERSION; }
+
+const char *retention_status_string(int s) {
+  switch (s) {
+    case RET_OK: return "ok";
+    case RET_ERR_INVALID_ARG: return "invalid argument";
+    case RET_ERR_UNSUPPORTED: return "unsupported";
+    case RET_ERR_WORKSPACE: return "workspace too small";
+    case RET_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char *retention_last_error(void) { return g_err; }
+
+ret_status_t retention_parallel(const void *q, const void *k, const void *v, void *o, int B, int H,
+                                int L, int dk, int dv, const float *gamma, const float *theta,
+                                long long pos0, float gn_eps, ret_dtype_t in_dtype,
+                                ret_dtype_t out_dtype, void *hip_stream) {
+  ret_status_t s = check_common(B, H, L, dk, dv, gamma, theta, pos0, gn_eps, in_dtype, out_dtype);
+  if (s != RET_OK) return s;
+  if (L == 0) return ok();
+  if (!q || !k || !v || !o) return fail(RET_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(RET_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const size_t nqk = (size_t)B * H * L * dk * esize(in_dtype), nv = (size_t)B * H * L * dv * esize(in_dtype);
+  const size_t no = (size_t)B * H * L * dv * esize(out_dtype);
+  if (overlap(o, no, q, nqk) || overlap(o, no, k, nqk) || overlap(o, no, v, nv))
+    return fail(RET_ERR_INVALID_ARG, "o overlaps an input");
+  RetArgs a = make_args(q, k, v, o, B, H, L, dk, dv, L, gamma, theta, pos0, gn_eps, in_dtype, out_dtype);
+  hipStream_t st = (hipStream_t)hip_stream;
+  if (use_mfma(dk, dv, in_dtype)) return hip_status(launch_mfma_parallel(a, st));
+  return hip_status(launch_vec_parallel(a, st));
+}
+
+size_t retention_chunkwise_workspace_bytes(int B, int H, int L, int dk, int dv, int chunk,
+                                           ret_dtype_t in_dtype) {
+  if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+  if (use_mfma(dk, dv, in_dtype)) return chunk_plan(B, H, L, dk, dv, chunk).ws_bytes;
+  return vec_chunk_ws(B, H, dk, dv);
+}
+
+ret_status_t retention_chunkwise(const void *q, const void *k, const void *v, void *o, int B, int H,
+                                 int L, int dk, int dv, int chunk, const float *gamma,
+                                 const float *theta, long long pos0, const float *state_in,
+                                 float *state_out, float gn_eps, ret_dtype_t in_dtype,
+                                 ret_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream) {
+  ret_status_t s = check_common(B, H, L, dk, dv, gamma, theta, pos0, gn_eps, in_dtype, out_dtype);
+  if (s != RET_OK) return s;
+  if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk=%d must be positive", chunk);
+  if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)))
+    return fail(RET_ERR_INVALID_ARG, "state pointers must be 16-byte aligned");
+  const size_t ns = (size_t)B * H * dk * dv * sizeof(float);
+  hipStream_t st = (hipStream_t)hip_stream;
+  if (L == 0) {  // nothing to compute: the state passes through unchanged
+    if (state_out && state_in && state_in != state_out && overlap(state_out, ns, state_in, ns))
+      return fail(RET_ERR_INVALID_ARG, "state_out partially overlaps state_in");
+    if (state_out) return hip_status(copy_or_zero(state_out, state_in, (long long)ns / 4, st));
+    return ok();
+  }
+  if (!q || !k || !v || !o) return fail(RET_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(RET_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const size_t nqk = (size_t)B * H * L * dk * esize(in_dtype), nv = (size_t)B * H * L * dv * esize(in_dtype);
+  const size_t no = (size_t)B * H * L * dv * esize(out_dtype);
+  if (overlap(o, no, q, nqk) || overlap(o, no, k, nqk) || overlap(o, no, v, nv))
+    return fail(RET_ERR_INVALID_ARG, "o overlaps an input");
+  if (state_out &&
+      (overlap(state_out, ns, q, nqk) || overlap(state_out, ns, k, nqk) || overlap(state_out, ns, v, nv) ||
+       overlap(state_out, ns, o, no) || (state_in && state_in != state_out && overlap(state_out, ns, state_in, ns))))
+    return fail(RET_ERR_INVALID_ARG, "state_out overlaps another tensor (only exact aliasing of state_in is allowed)");
+  RetArgs a = make_args(q, k, v, o, B, H, L, dk, dv, chunk, gamma, theta, pos0, gn_eps, in_dtype, out_dtype);
+  if (use_mfma(dk, dv, in_dtype)) {
+    ChunkPlan plan = chunk_plan(B, H, L, dk, dv, chunk);
+    if (plan.ws_bytes && (!workspace || workspace_bytes < plan.ws_bytes))
+      return fail(RET_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes, workspace_bytes);
+    if (workspace && !aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return hip_status(launch_mfma_chunkwise(a, plan, workspace, state_in, state_out, st));
+  }
+  // vector path: the running state lives in state_out when given, else in the workspace
+  float *S = state_out;
+  if (!S) {
+    const size_t need = vec_chunk_ws(B, H, dk, dv);
+    if (!workspace || workspace_bytes < need)
+      return fail(RET_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (!aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    S = (float *)workspace;
+  }
+  return hip_status(launch_vec_chunkwise(a, S, state_in, st));
+}
+
+ret_status_t retention_recurrent_step(const void *q, const void *k, const void *v, float *state,
+                                      void *o, int B, int H, int dk, int dv, const float *gamma,
+                                      const float *theta, const int *pos, float gn_eps,
+                                      ret_dtype_t in_dtype, ret_dtype_t out_dtype, void *hip_stream) {
+  ret_status_t s = check_common(B, H, 1, dk, dv, gamma, theta, 0, gn_eps, in_dtype, out_dtype);
+  if (s != RET_OK) return s;
+  if (!q || !k || !v || !o || !state) return fail(RET_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (theta && !pos) return fail(RET_ERR_INVALID_ARG, "pos is NULL but rotation is on");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state))
+    return fail(RET_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (!(dv % 4 == 0 ? dv / 4 <= 256 : dv <= 256))
+    return fail(RET_ERR_UNSUPPORTED, "dv=%d: the step kernel needs dv %% 4 == 0 or dv <= 256", dv);
+  const size_t ns = (size_t)B * H * dk * dv * sizeof(float);
+  const size_t nqk = (size_t)B * H * dk * esize(in_dtype), nv = (size_t)B * H * dv * esize(in_dtype);
+  const size_t no = (size_t)B * H * dv * esize(out_dtype);
+  if (overlap(o, no, q, nqk) || overlap(o, no, k, nqk) || overlap(o, no, v, nv) || overlap(o, no, state, ns) ||
+      overlap(state, ns, q, nqk) || overlap(state, ns, k, nqk) || overlap(state, ns, v, nv))
+    return fail(RET_ERR_INVALID_ARG, "state or o overlaps another tensor");
+  RetArgs a = make_args(q, k, v, o, B, H, 1, dk, dv, 1, gamma, theta, 0, gn_eps, in_dtype, out_dtype);
+  a.q_sn = a.q_sh = dk;
+  a.q_sb = (long long)H * dk;
+  a.v_sn = a.v_sh = a.o_sn = a.o_sh = dv;
+  a.v_sb = a.o_sb = (long long)H * dv;
+  return hip_status(launch_vec_step(a, state, pos, (hipStream_t)hip_stream));
+}
+
+}  // extern "C"

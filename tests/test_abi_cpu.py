@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch (so no
+call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import retentive_network_scale_amd as rn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "retention.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+F32, BF16 = 0, 1
+FAKE = ctypes.c_void_p(0x100000)      # never dereferenced: every call below fails validation
+FAKE2 = ctypes.c_void_p(0x200000)
+FAKE3 = ctypes.c_void_p(0x300000)
+FAKE4 = ctypes.c_void_p(0x400000)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(retention_\w+|msr_\w+)\s*\(", src)))
+
+
+def _f(vals):
+    return (ctypes.c_float * len(vals))(*vals)
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "retention_parallel" in names and "msr_layer_fwd" in names
+    L = rn.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in rn.EXPORTED_SYMBOLS, f"binding does not wrap {n}"
+    assert set(rn.EXPORTED_SYMBOLS) == set(names)
+
+
+def test_version_and_status_strings():
+    L = rn.lib()
+    assert L.retention_abi_version() == 1
+    assert L.retention_status_string(0) == b"ok"
+    assert L.retention_status_string(3) == b"workspace too small"
+
+
+def _par(**kw):
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, B=1, H=2, L=8, dk=16, dv=16, gamma=_f([0.9, 0.5]),
+             theta=None, pos0=0, eps=-1.0, ind=F32, outd=F32)
+    a.update(kw)
+    return rn.lib().retention_parallel(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["L"], a["dk"],
+                                       a["dv"], a["gamma"], a["theta"], a["pos0"], a["eps"], a["ind"],
+                                       a["outd"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(dk=0), INVALID), (dict(L=-3), INVALID),
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(gamma=None), INVALID),
+    (dict(gamma=_f([1.5, 0.5])), INVALID), (dict(gamma=_f([float("nan"), 0.5])), INVALID),
+    (dict(gamma=_f([-0.1, 0.5])), INVALID),
+    (dict(dk=15, theta=_f([1.0] * 7)), INVALID), (dict(theta=_f([1.0] * 7 + [float("inf")])), INVALID),
+    (dict(eps=float("nan")), INVALID), (dict(eps=float("inf")), INVALID),
+    (dict(ind=7), INVALID), (dict(pos0=-1), INVALID),
+    (dict(q=ctypes.c_void_p(0x100004)), INVALID),   # misaligned
+    (dict(o=FAKE), INVALID),                        # output aliases an input
+    (dict(H=129, gamma=_f([0.5] * 129)), UNSUPPORTED), (dict(dv=2048), UNSUPPORTED),
+])
+def test_parallel_rejects(kw, code):
+    assert _par(**kw) == code
+    assert rn.lib().retention_last_error() != b""
+
+
+def test_empty_sequence_is_a_noop():
+    assert _par(L=0, q=None, k=None, v=None, o=None) == 0
+
+
+def test_chunkwise_rejects_and_workspace():
+    L = rn.lib()
+    g = _f([0.9, 0.5])
+    need = L.retention_chunkwise_workspace_bytes(1, 2, 64, 16, 16, 16, F32)
+    assert need > 0
+    call = lambda chunk=16, ws=None, wsb=0, so=None: L.retention_chunkwise(
+        FAKE, FAKE2, FAKE3, FAKE4, 1, 2, 64, 16, 16, chunk, g, None, 0, None, so, -1.0, F32, F32, ws,
+        wsb, None)
+    assert call(chunk=0) == INVALID
+    assert call() == WORKSPACE                      # no state_out: the state needs the workspace
+    assert call(ws=FAKE, wsb=need - 1) == WORKSPACE
+    assert call(so=FAKE) == INVALID                 # state_out overlaps q
+    assert L.retention_chunkwise_workspace_bytes(0, 2, 64, 16, 16, 16, F32) == 0
+
+
+def test_recurrent_step_rejects():
+    L = rn.lib()
+    g = _f([0.9, 0.5])
+    th = _f([1.0] * 8)
+    st = ctypes.c_void_p(0x500000)
+    base = dict(q=FAKE, k=FAKE2, v=FAKE3, s=st, o=FAKE4, th=None, pos=None, dv=16)
+
+    def call(**kw):
+        a = dict(base); a.update(kw)
+        return L.retention_recurrent_step(a["q"], a["k"], a["v"], a["s"], a["o"], 2, 2, 16, a["dv"], g,
+                                          a["th"], a["pos"], -1.0, F32, F32, None)
+    assert call(s=None) == INVALID
+    assert call(th=th) == INVALID                  # rotation needs positions
+    assert call(dv=1022) == UNSUPPORTED
+    assert call(o=st) == INVALID                    # o aliases the state
+
+
+def test_msr_rejects_unsupported_shapes():
+    L = rn.lib()
+    g = _f([0.9] * 2)
+    r = L.msr_layer_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, 1, 8, 40, 2, 24, 24, 8, g, None, 0,
+                        1e-5, None, 0, None)
+    assert r in (INVALID, UNSUPPORTED)
