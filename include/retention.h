@@ -82,7 +82,7 @@ const char *retention_last_error(void);
  * D_nm = gamma_h^(n-m) for n >= m, else 0; then the optional GroupNorm.
  *   q, k : [B,H,L,dk] in_dtype          v : [B,H,L,dv] in_dtype
  *   o    : [B,H,L,dv] out_dtype (must not alias an input)
- * bf16 inputs with (dk, dv) in {(64,64),(64,128),(128,128),(128,256),(256,256),
+ * bf16 inputs with (dk, dv) in {(64,128),(128,128),(128,256),(256,256),
  * (256,512)} use the MFMA kernels; every other case uses the vector (FMA) kernels.
  * L == 0 is a no-op.
  */

@@ -129,6 +129,13 @@ size_t vec_chunk_ws(int B, int H, int dk, int dv) { return (size_t)B * H * dk * 
 
 }  // namespace
 
+// Records the per-thread message of retention_last_error() for the other
+// translation units (the layer); RET_OK clears it.
+ret_status_t retention_fail_(ret_status_t s, const char *msg) {
+  if (s == RET_OK) return ok();
+  return fail(s, "%s", msg);
+}
+
 extern "C" {
 
 int retention_abi_version(void) { return RETENTION_ABI_VERSION; }

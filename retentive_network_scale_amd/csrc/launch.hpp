@@ -28,14 +28,28 @@ ChunkPlan chunk_plan(int B, int H, int L, int dk, int dv, int chunk);
 hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &plan, void *ws,
                                  const float *state_in, float *state_out, hipStream_t st);
 
-// bf16 GEMM: C[M][N] = A[M][K] . W^T with W stored [N][K]; see gemm.hip for epilogues.
-struct GemmEpilogue {
-  int kind;              // 0: plain bf16 row-major store; 1: head-major scatter; 2: swish
-  void *out;
-  long long ld_out;      // row stride of out (kind 0, 2)
-  int L, H, dh;          // kind 1: row r = (b, l), column c = (h, j) -> out[((b*H+h)*L+l)*dh+j]
+// bf16 GEMM: C[M][N] = A[M][K] . W^T with W stored [N][K]; see gemm.hip.
+// Requires K % 64 == 0 and every segment's n % 128 == 0.
+enum { GEMM_PLAIN = 0, GEMM_HEADS = 1, GEMM_SWISH = 2 };
+struct GemmSeg {
+  const uint16_t *w;  // [n][K]
+  int n;              // output columns of this segment
+  int kind;           // GEMM_PLAIN / GEMM_HEADS / GEMM_SWISH
+  void *out;          // bf16
+  long long ld;       // row stride of out (PLAIN, SWISH)
+  int L, H, dh;       // HEADS: rows are (b, l) with l < L; columns (h, j) with j < dh
 };
-hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *W, int M, int N, int K,
-                            const GemmEpilogue &ep, hipStream_t st);
+struct GemmArgs {
+  const uint16_t *A;  // [M][K]
+  int M, K;
+  int nseg;
+  GemmSeg seg[4];
+  int n_total, ntiles;  // filled by the launcher
+};
+hipError_t launch_gemm_bf16(const GemmArgs &args, hipStream_t st);
+
+// GroupNorm of rows of a [B, L, H, dv]-strided fp32 tensor, times an optional
+// bf16 gate, written as bf16 with the same strides (gated layer).
+hipError_t launch_gn_gate(const RetArgs &a, const float *o32, uint16_t *z, hipStream_t st);
 
 }  // namespace ret

@@ -1,0 +1,134 @@
+"""GPU parity of the bf16 MFMA retention kernels against the fp64 oracle (C ABI).
+
+Shapes span several 64-token tiles with ragged tails, every supported head-size
+pair, rotation on/off, GroupNorm on/off, fp32 and bf16 outputs, chunk sizes that
+do and do not divide L, several chunks per segment (state carried inside a
+workgroup) and several segments (state carried by the scan), incoming state and
+aliased state_in/state_out.  bf16 bar: rel-L2 <= 2e-2, unit-normalised max-abs
+<= 5e-2, per (b, h) slice.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import retentive_network_scale_amd as rn
+from tests import _tol
+from workloads import multiscale_gamma, randn, rotation_theta
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+PAIRS = [(64, 128), (128, 128), (128, 256), (256, 256), (256, 512)]
+
+
+def _qkv(B, H, L, dk, dv, seed):
+    s = 1.0 / np.sqrt(dk)
+    return (randn((B, H, L, dk), seed, s, torch.bfloat16), randn((B, H, L, dk), seed + 1, s, torch.bfloat16),
+            randn((B, H, L, dv), seed + 2, 1.0, torch.bfloat16))
+
+
+def _gpu(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+@pytest.mark.parametrize("dk,dv", PAIRS)
+@pytest.mark.parametrize("rot,gn,odt", [(True, None, torch.bfloat16), (False, 1e-5, torch.float32),
+                                        (True, 1e-5, torch.bfloat16)])
+def test_parallel_mfma(dk, dv, rot, gn, odt):
+    B, H, L = 2, 3, 200
+    q, k, v = _qkv(B, H, L, dk, dv, 100 + dk + dv)
+    g = multiscale_gamma(H)
+    th = rotation_theta(dk) if rot else None
+    ref = oracle.parallel(q, k, v, g, th, pos0=37)
+    if gn is not None:
+        ref = oracle.groupnorm(ref, gn)
+    o = rn.retention_parallel(*_gpu(q, k, v), g, th, pos0=37, gn_eps=gn, out_dtype=odt)
+    torch.cuda.synchronize()
+    assert o.dtype == odt
+    _tol.assert_bf16(o, ref, what=f"parallel dk={dk} dv={dv} rot={rot} gn={gn}")
+
+
+@pytest.mark.parametrize("dk,dv", PAIRS)
+@pytest.mark.parametrize("L,chunk", [(300, 64), (300, 100), (130, 256)])
+def test_chunkwise_mfma(dk, dv, L, chunk):
+    B, H = 1, 2
+    q, k, v = _qkv(B, H, L, dk, dv, 200 + dk + dv + chunk)
+    s0 = randn((B, H, dk, dv), 7, 0.5)
+    g = torch.tensor([0.97, 0.5], dtype=torch.float32)
+    th = rotation_theta(dk)
+    ref_o, ref_s = oracle.recurrent(q, k, v, g, th, pos0=11, s_in=s0)
+    qd, kd, vd, sd = _gpu(q, k, v, s0)
+    o, s = rn.retention_chunkwise(qd, kd, vd, g, chunk, th, pos0=11, state_in=sd, state_out=True,
+                                  out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _tol.assert_bf16(o, ref_o, what=f"chunkwise dk={dk} dv={dv} L={L} chunk={chunk}")
+    _tol.assert_bf16(s, ref_s, what="final state")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 256), (256, 512)])
+def test_chunkwise_segments_and_carry(dk, dv):
+    """B*H = 32 units so that every head gets several segments of several chunks
+    (state carried in registers inside a segment and by the scan across them);
+    GroupNorm on; state_out aliases state_in."""
+    B, H, L, chunk = 4, 8, 1100, 64
+    q, k, v = _qkv(B, H, L, dk, dv, 300 + dk)
+    s0 = randn((B, H, dk, dv), 8, 0.3)
+    g, th = multiscale_gamma(H), rotation_theta(dk)
+    ref_o, ref_s = oracle.recurrent(q, k, v, g, th, pos0=5, s_in=s0)
+    ref_gn = oracle.groupnorm(ref_o, 1e-5)
+    qd, kd, vd, sd = _gpu(q, k, v, s0)
+    o, s = rn.retention_chunkwise(qd, kd, vd, g, chunk, th, pos0=5, state_in=sd, state_out=sd, gn_eps=1e-5)
+    torch.cuda.synchronize()
+    _tol.assert_bf16(o, ref_gn, what="chunkwise+GN")
+    _tol.assert_bf16(sd, ref_s, what="aliased final state")
+
+
+def test_chunk_size_independence_gpu():
+    """Outputs and the final state agree across chunk sizes (and with the parallel kernel)."""
+    B, H, L, dk, dv = 1, 4, 512, 128, 256
+    q, k, v = _qkv(B, H, L, dk, dv, 400)
+    g, th = multiscale_gamma(H), rotation_theta(dk)
+    qd, kd, vd = _gpu(q, k, v)
+    ref = oracle.recurrent(q, k, v, g, th)[0]
+    par = rn.retention_parallel(qd, kd, vd, g, th, out_dtype=torch.float32)
+    _tol.assert_bf16(par, ref, what="parallel")
+    states = []
+    for chunk in (64, 128, 256, 512, 1000):
+        o, s = rn.retention_chunkwise(qd, kd, vd, g, chunk, th, state_out=True, out_dtype=torch.float32)
+        _tol.assert_bf16(o, ref, what=f"chunk {chunk}")
+        states.append(s)
+    torch.cuda.synchronize()
+    for s in states[1:]:
+        _tol.assert_bf16(s, states[0], what="state vs chunk 64")
+
+
+def test_mask_extraction_mfma():
+    """theta = 0, q = k = e_0, v_m = e_m (exact in bf16): o[n][m] = D[n][m] up to the
+    bf16 rounding of the decayed scores."""
+    L, dk, dv = 128, 64, 128
+    q = torch.zeros((1, 1, L, dk), dtype=torch.bfloat16); q[..., 0] = 1.0
+    v = torch.zeros((1, 1, L, dv), dtype=torch.bfloat16)
+    v[0, 0, torch.arange(L), torch.arange(L)] = 1.0
+    gm = 1 - 2 ** -5
+    o = rn.retention_parallel(*_gpu(q, q.clone(), v), [gm], out_dtype=torch.float32)
+    oc, _ = rn.retention_chunkwise(*_gpu(q, q.clone(), v), [gm], 64, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    n, m = np.meshgrid(np.arange(L), np.arange(L), indexing="ij")
+    D = np.where(n >= m, gm ** np.maximum(n - m, 0), 0.0)
+    for out in (o, oc):
+        got = out[0, 0].double().cpu().numpy()
+        assert np.all(got[n < m] == 0.0)
+        assert np.all(got[n == m] == 1.0)
+        assert np.abs(got - D).max() <= 2 ** -8
+
+
+def test_gamma_edges_mfma():
+    """gamma = 0 (identity decay) and gamma = 1 (causal linear attention) through the MFMA path."""
+    B, H, L, dk, dv = 1, 2, 150, 64, 128
+    q, k, v = _qkv(B, H, L, dk, dv, 500)
+    g = torch.tensor([0.0, 1.0])
+    ref = oracle.parallel(q, k, v, g)
+    qd, kd, vd = _gpu(q, k, v)
+    _tol.assert_bf16(rn.retention_parallel(qd, kd, vd, g, out_dtype=torch.float32), ref, what="parallel")
+    o, _ = rn.retention_chunkwise(qd, kd, vd, g, 64, out_dtype=torch.float32)
+    _tol.assert_bf16(o, ref, what="chunkwise")
