@@ -1,0 +1,249 @@
+"""Benchmark of the MI355X retention library on one GPU.
+
+Headline (`value`): chunkwise retention tokens/s on the long-context workload
+(B1 H8 L32768 dk128 dv256, chunk 256, bf16 in and out, final state written),
+inputs resident in HBM.  One step = one retention_chunkwise call.  The same JSON
+line also carries the recurrent decode rate (B128 H16 dk128 dv256, 1024 steps
+after a 512-token prefill), the parallel-form and MSR-layer rates, each with its
+roofline, and the fp64 CPU oracle timed on a bounded sample of the headline
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunkwise retention tokens/s @L=32K; recurrent decode tokens/s; % roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _time_calls(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1000.0  # seconds for all steps
+
+
+def _read_traffic(name):
+    """HBM bytes per call from a committed rocprofv3 PMC summary, or None if it
+    is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("src_sha") != _src_sha():
+            return None
+        return float(kv["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _src_sha():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "retentive_network_scale_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def bench_chunkwise(steps, warmup):
+    import torch
+    import retentive_network_scale_amd as rn
+    from workloads import CHUNKWISE_32K as wl
+    q, k, v = (t.cuda() for t in wl.qkv())
+    g, th = wl.gamma(), wl.theta()
+    out = torch.empty((wl.B, wl.H, wl.L, wl.dv), dtype=torch.bfloat16, device="cuda")
+    state = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(rn.retention_chunkwise_workspace_bytes(wl.B, wl.H, wl.L, wl.dk, wl.dv, wl.chunk),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        rn.retention_chunkwise(q, k, v, g, wl.chunk, th, state_out=state, out=out, workspace=ws)
+    t = _time_calls(call, steps, warmup)
+    per_call = t / steps
+    tokens = wl.B * wl.L
+    # algorithmic: Q, K, V read once, O (bf16) and the final fp32 state written once
+    bytes_alg = 2 * (2 * wl.B * wl.H * wl.L * wl.dk) + 2 * wl.B * wl.H * wl.L * wl.dv * 2 + \
+        4 * wl.B * wl.H * wl.dk * wl.dv
+    C = wl.chunk
+    flops_alg = wl.B * wl.H * (wl.L / C) * 2 * (C * (C + 1) / 2 * (wl.dk + wl.dv) + 2 * C * wl.dk * wl.dv)
+    achieved = bytes_alg / per_call / 1e9
+    traffic = _read_traffic("chunkwise_32k")
+    return {
+        "tokens_per_s": tokens / per_call, "ms_per_step": per_call * 1e3, "tokens": tokens,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "retention_chunkwise (seg_state + seg_scan + tile_kernel launches)",
+                     "algorithmic_bytes_per_call": bytes_alg},
+        "mfma": {"algorithmic_tflop_per_call": flops_alg / 1e12,
+                 "achieved_tflops": flops_alg / per_call / 1e12,
+                 "frac_of_bf16_peak": flops_alg / per_call / 1e12 / BF16_PEAK_TFLOPS},
+    }
+
+
+def bench_decode(warmup_loops=1):
+    import torch
+    import retentive_network_scale_amd as rn
+    from workloads import DECODE as wl
+    g, th = wl.gamma(), wl.theta()
+    pq, pk, pv = (t.cuda() for t in wl.prefill_qkv())
+    sq, sk, sv = (t.cuda() for t in wl.step_qkv())
+    state = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    pos_all = (torch.arange(wl.steps, dtype=torch.int32) + wl.prefill).reshape(-1, 1).expand(-1, wl.B)
+    pos_all = pos_all.contiguous().cuda()
+    outs = torch.empty((wl.steps, wl.B, wl.H, wl.dv), dtype=torch.bfloat16, device="cuda")
+    qs, ks, vs, ps, os_ = ([x[t] for t in range(wl.steps)] for x in (sq, sk, sv, pos_all, outs))
+
+    def prefill():
+        rn.retention_chunkwise(pq, pk, pv, g, wl.chunk, th, state_out=state)
+
+    def loop():
+        for t in range(wl.steps):
+            rn.retention_recurrent_step(qs[t], ks[t], vs[t], state, ps[t], g, th, out=os_[t])
+    for _ in range(warmup_loops):
+        prefill()
+        loop()
+    prefill()
+    torch.cuda.synchronize()
+    t = _time_calls(loop, 1, 0)
+    per_step = t / wl.steps
+    bytes_step = 2 * 4 * wl.B * wl.H * wl.dk * wl.dv + 2 * 2 * wl.B * wl.H * wl.dk + 2 * 2 * wl.B * wl.H * wl.dv
+    achieved = bytes_step / per_step / 1e9
+    return {"tokens_per_s": wl.B * wl.steps / t, "ms_per_step": per_step * 1e3, "steps": wl.steps,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": _read_traffic("decode_step"),
+                         "kernel": "vec_step_kernel (one launch per step; launch gaps included)",
+                         "algorithmic_bytes_per_call": bytes_step}}
+
+
+def bench_parallel(steps, warmup):
+    import torch
+    import retentive_network_scale_amd as rn
+    from workloads import PARALLEL_2K as wl
+    q, k, v = (t.cuda() for t in wl.qkv())
+    g, th = wl.gamma(), wl.theta()
+    out = torch.empty((wl.B, wl.H, wl.L, wl.dv), dtype=torch.bfloat16, device="cuda")
+    t = _time_calls(lambda: rn.retention_parallel(q, k, v, g, th, gn_eps=wl.gn_eps, out=out), steps, warmup)
+    per_call = t / steps
+    flops = 2 * wl.B * wl.H * wl.L * (wl.L + 1) / 2 * (wl.dk + wl.dv)
+    tf = flops / per_call / 1e12
+    return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": _read_traffic("parallel_2k"),
+                         "kernel": "tile_kernel<256,512,parallel,split>",
+                         "algorithmic_tflop_per_call": flops / 1e12}}
+
+
+def bench_msr(steps, warmup):
+    import torch
+    import retentive_network_scale_amd as rn
+    from workloads import MSR_LAYER as wl
+    x, wq, wk, wv, wg, wo = (t.cuda() for t in wl.inputs())
+    g, th = wl.gamma(), wl.theta()
+    y = torch.empty((wl.B, wl.L, wl.d_model), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(rn.msr_layer_fwd_workspace_bytes(wl.B, wl.L, wl.d_model, wl.H, wl.dk, wl.dv, wl.chunk),
+                     dtype=torch.uint8, device="cuda")
+    t = _time_calls(lambda: rn.msr_layer_fwd(x, wq, wk, wv, wg, wo, wl.H, wl.dk, wl.dv, wl.chunk, g, th,
+                                             gn_eps=wl.gn_eps, out=y, workspace=ws), steps, warmup)
+    per_call = t / steps
+    T = wl.B * wl.L
+    C = wl.chunk
+    gemm = 2 * T * wl.d_model * (2 * wl.H * wl.dk + 2 * wl.H * wl.dv) + 2 * T * wl.H * wl.dv * wl.d_model
+    ret = T * wl.H * ((C + 1) * (wl.dk + wl.dv) + 4 * wl.dk * wl.dv)
+    tf = (gemm + ret) / per_call / 1e12
+    return {"tokens_per_s": T / per_call, "ms_per_step": per_call * 1e3,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                         "kernel": "msr_layer_fwd (GEMM, chunkwise retention, GroupNorm+gate, GEMM)",
+                         "algorithmic_tflop_per_call": (gemm + ret) / 1e12}}
+
+
+def cpu_baseline(sample_tokens):
+    """The fp64 oracle (chunkwise form, chunk 256) on the first `sample_tokens`
+    tokens of all 8 heads of the long-context workload, timed on host cores."""
+    import oracle
+    from workloads import CHUNKWISE_32K as wl
+    q, k, v = wl.qkv()
+    n = sample_tokens
+    qs, ks, vs = (oracle.as_f64(t[:, :, :n]) for t in (q, k, v))
+    g, th = wl.gamma(), wl.theta()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.chunkwise(qs, ks, vs, g, wl.chunk, th)
+    dt = time.perf_counter() - t0
+    return {"value": wl.B * n / dt, "unit": "tokens/s", "cores": min(threads, wl.B * wl.H), "kind": "oracle",
+            "sample": f"fp64 chunkwise oracle (chunk {wl.chunk}) on tokens 0..{n - 1} of all {wl.H} heads of "
+                      f"the L=32768 workload, {dt:.1f} s; OpenMP over the {wl.B * wl.H} (b, h) units"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="headline chunkwise workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import retentive_network_scale_amd as rn
+    rn.lib()  # fails loudly if the HIP library is not built
+    from workloads import CHUNKWISE_32K
+    _log("chunkwise L=32768")
+    ch = bench_chunkwise(args.steps, args.warmup)
+    line = {
+        "metric": METRIC, "value": ch["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ch["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": CHUNKWISE_32K.name, "batch": CHUNKWISE_32K.B, "seq_len": CHUNKWISE_32K.L,
+                   "heads": CHUNKWISE_32K.H, "dk": CHUNKWISE_32K.dk, "dv": CHUNKWISE_32K.dv,
+                   "chunk": CHUNKWISE_32K.chunk},
+        "roofline": ch["roofline"], "chunkwise_mfma": ch["mfma"],
+    }
+    if not args.no_extra:
+        _log("decode B128 H16, 1024 steps")
+        line["decode"] = bench_decode()
+        _log("parallel B8 H8 L2048")
+        line["parallel"] = bench_parallel(max(3, args.steps // 2), args.warmup)
+        _log("msr layer B4 L4096")
+        line["msr_layer"] = bench_msr(max(3, args.steps // 4), args.warmup)
+    if not args.no_cpu:
+        _log(f"cpu baseline ({args.cpu_tokens} tokens)")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
