@@ -33,17 +33,16 @@ struct RetArgs {
 // ------------------------------------------------------------------ numerics
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __attribute__((ext_vector_type(2))) float ret_f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 ret_bf16x2;
+
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even, NaN kept:
+// one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(ret_f32x2{lo, hi}, ret_bf16x2));
 }
 
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-}
+__device__ __forceinline__ uint16_t f2bf(float f) { return (uint16_t)(pack_bf2(f, 0.0f) & 0xffffu); }
 
 __device__ __forceinline__ float load_elem(const void *p, long long i, int is_bf16) {
   return is_bf16 ? bf2f(((const uint16_t *)p)[i]) : ((const float *)p)[i];

@@ -20,9 +20,12 @@ bool mfma_supported(int dk, int dv);
 hipError_t launch_mfma_parallel(const RetArgs &a, hipStream_t st);
 // Chunkwise form.  Workspace layout and size come from chunk_plan().
 struct ChunkPlan {
-  int seg_chunks;     // chunks per segment (one block per segment)
+  int seg_chunks;     // chunks per segment
   int nseg;           // segments per (b, h)
-  size_t ws_bytes;    // segment-state workspace
+  size_t seg_bytes;   // fp32 segment states [B*H][nseg][dk][dv]
+  size_t sinT_bytes;  // bf16 incoming segment states, transposed [B*H][nseg][dv][dk]
+  size_t loc_bytes;   // bf16 local chunk states, transposed [B*H][nchunks][dv][dk]
+  size_t ws_bytes;    // total
 };
 ChunkPlan chunk_plan(int B, int H, int L, int dk, int dv, int chunk);
 hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &plan, void *ws,
@@ -47,9 +50,5 @@ struct GemmArgs {
   int n_total, ntiles;  // filled by the launcher
 };
 hipError_t launch_gemm_bf16(const GemmArgs &args, hipStream_t st);
-
-// GroupNorm of rows of a [B, L, H, dv]-strided fp32 tensor, times an optional
-// bf16 gate, written as bf16 with the same strides (gated layer).
-hipError_t launch_gn_gate(const RetArgs &a, const float *o32, uint16_t *z, hipStream_t st);
 
 }  // namespace ret

@@ -18,11 +18,10 @@
 // transposed, O^T[dv][query], so that:
 //   * the decayed scores S^T = K Q^T come out of the MFMA in the lane layout
 //     of the B operand of O^T += V^T P^T (no register shuffles),
-//   * the fp32 state S[dk][dv], kept in MFMA accumulators, is already in the
-//     lane layout of the A operand of the cross term O^T += S^T Q^T.
-// Every wave owns RW = DVW/8 rows of O^T (dv) and the matching columns of the
-// state.  Scores of a 64x64 block are split over the 8 waves (16 queries x 32
-// keys each) and shared through LDS in bf16.
+//   * a chunk state stored as bf16 S^T[dv][dk] is directly the A operand of
+//     the cross term O^T += S^T Q^T.
+// Every wave owns RW = DV/8 rows of O^T (dv).  Scores of a 64x64 block are
+// split over the 8 waves (16 queries x 32 keys each) and shared through LDS.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16.  Lane l, g = l/16: A holds A[l%16][K-set],
 // B holds B[K-set][l%16], D holds D[4g+i][l%16].  The K-set of lane group g in
@@ -30,12 +29,17 @@
 // B gives the same product, and this one maps a pair of D blocks straight
 // onto an operand.
 //
-// Chunkwise runs as three launches (the cross-chunk carry over segments):
+// Chunkwise runs as three launches (the cross-chunk carry over segments of
+// whole chunks):
 //   1. seg_state: per (b, h, segment, dv slice) the segment's own state
 //      sum_t gamma^(s1-1-t) k_t^T v_t  (zero incoming state) -> workspace;
 //   2. seg_scan : per state element, S_in(s+1) = gamma^len(s) S_in(s) + dS(s),
 //      written back in place (exclusive) plus the final state;
-//   3. seg_out  : per segment, the chunk loop above, starting from S_in.
+//   3. seg_out  : per segment, the chunk loop, starting from S_in, with the
+//      fp32 state in MFMA accumulators (it is then also the A operand of the
+//      cross term, converted to bf16).
+// The parallel form is the query-block kernel: one task per (b, h, 64-query
+// block), key blocks up to the diagonal, no state.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -48,7 +52,11 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int NT = 512;   // threads per workgroup
 constexpr int BT = 64;    // query / key block (tokens)
-constexpr int LDT = BT + 8;  // row length (bf16) of token-minor LDS tiles
+// LDS row lengths (bf16).  MFMA operands are read as 8-byte pieces from 16
+// consecutive rows; a row stride of 34 dwords (mod 32: 2) puts those 16 reads
+// on 32 distinct banks.  Rows are therefore only 8-byte aligned and every LDS
+// access is at most 8 bytes wide.
+constexpr int LDT = BT + 4;  // token-minor tiles (Vt, Kt, Ps): 136 bytes
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -67,8 +75,30 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
 }
 
 // gamma^d for integer d >= 0, d == 0 -> 1 (so gamma = 0 gives the identity).
+// Raw v_exp_f32: results below the fp32 normal range flush to 0, far below any
+// term they would be added to.
 __device__ __forceinline__ float dpow(float lg2, int d) {
-  return d == 0 ? 1.0f : exp2f((float)d * lg2);
+  return d == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)d * lg2);
+}
+
+// Rotation table for a kernel: rev_s[i] = theta_i / (2 pi) in fp32, th_s[i] = theta_i.
+// A tile starting at absolute position P0 needs, per pair i, the fp64-reduced
+// base A_i = frac(P0 theta_i / 2pi); token t of the tile then has angle (in
+// revolutions) frac(A_i + t * rev_s[i]), t < 64, so the fp32 part stays small.
+__device__ __forceinline__ float base_rev(long long p0, float theta) {
+  double r = (double)p0 * (double)theta * 0.15915494309189535;
+  return (float)(r - rint(r));
+}
+
+// Decay table of one head in LDS: dt[x + 64] = gamma^x for 0 <= x < 128 and 0
+// for -64 <= x < 0, so a lookup also applies the causal mask.  For a query block
+// starting at q0 and a key block at k0 = q0 - 64*delta, the distance of query
+// q0+n' and key k0+m' is 64*delta + d' with d' = n' - m' in [-63, 63]:
+//   delta == 0: gamma^d' or 0 (masked) = dt[d' + 64]
+//   delta >= 1: gamma^(64(delta-1)) * gamma^(d'+64), and d' + 64 is in [1, 127]
+constexpr int DT_SZ = 192;
+__device__ __forceinline__ void fill_decay_table(float *dt, float lg, int nthreads) {
+  for (int i = threadIdx.x; i < DT_SZ; i += nthreads) dt[i] = i < 64 ? 0.0f : dpow(lg, i - 64);
 }
 
 template <int DK, int DVW>
@@ -77,86 +107,183 @@ struct Tile {
   static constexpr int RB = RW / 16;   // 16-row blocks per wave
   static constexpr int KS = DK / 32;   // k-steps over dk
   static constexpr int DKB = DK / 16;  // 16-row blocks of dk
-  static constexpr int LDQ = DK + 8;   // row length (bf16) of token-major LDS tiles
+  static constexpr int LDQ = DK + 4;   // token-major tiles (Qs, Ks): 2*DK + 8 bytes
   static_assert(RW % 16 == 0 && DK % 32 == 0, "tile shape");
 };
 
-// Stage a 64-token block of a [tokens][D] bf16 tensor into LDS.
-//   rows (if ROWS): dst[r][0..D)   (token-major, row length D+8)
-//   trans (if TRANS): dstT[d][0..64) (token-minor, row length LDT), scaled per token by zeta
-// Tokens at or beyond `valid` are zero.  Rotation (ROT) by the xPOS phase at
-// absolute position pos_base + r uses the fp32 theta table in LDS.
-template <int D, bool ROWS, bool TRANS, bool ROT, bool LO = false>
-__device__ __forceinline__ void stage(const uint16_t *src, long long stride, int valid,
-                                      long long pos_base, const float *theta_s, uint16_t *dst,
-                                      uint16_t *dstT, const float *zeta, uint16_t *dstLo = nullptr) {
-  constexpr int C8 = D / 8;
-  for (int idx = threadIdx.x; idx < 16 * C8; idx += NT) {
-    const int c8 = idx % C8, kq = idx / C8;
-    float x[4][8];
+// Moving a 64-token tile of a [tokens][D] bf16 tensor from HBM to LDS, in two
+// steps so that the global loads of the next tile overlap the MFMA work on the
+// current one: fetch() issues 16-byte loads into registers, commit() converts
+// them (rotation, per-token scale) and writes LDS.
+//
+// Thread mapping: work item = (token group tg, 16-byte column chunk c8), tg
+// fastest across lanes; a thread holds TPT consecutive tokens of one chunk.
+// The transposed (token-minor) LDS write of a column then covers TPT tokens in
+// one 4/8/16-byte store, and consecutive lanes write consecutive addresses of
+// the same LDS row: no bank conflicts.  Each global row segment read by a wave
+// is 64 bytes or more and fully used.
+template <int D>
+struct TileIO {
+  static constexpr int C8 = D / 8;
+  static constexpr int TPT = (C8 / 8 < 2) ? 2 : C8 / 8;  // tokens per thread
+  static constexpr int NG = BT / TPT;                     // token groups
+  static constexpr int ITEMS = NG * C8;
+  static constexpr int NI = (ITEMS + NT - 1) / NT;
+  static constexpr int CG = 4;  // consecutive lanes on consecutive chunks of a row: 64-byte global segments
+  static_assert(TPT == 2 || TPT == 4 || TPT == 8, "tokens per thread");
+  static_assert(C8 % CG == 0, "column chunks");
+  uint4 raw[NI][TPT];
+
+  __device__ __forceinline__ static void item(int idx, int &tg, int &c8) {
+    const int lo = idx % CG, rest = idx / CG;
+    tg = rest % NG;
+    c8 = (rest / NG) * CG + lo;
+  }
+
+  __device__ __forceinline__ void fetch(const uint16_t *src, long long stride, int valid) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = 4 * kq + rr;
-      if (r < valid) {
-        const uint4 u = *(const uint4 *)(src + (long long)r * stride + 8 * c8);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int i = 0; i < NI; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      int tg, c8;
+      item(idx, tg, c8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[rr][2 * e] = __uint_as_float(w[e] << 16);
-          x[rr][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-        }
-        if constexpr (ROT) {
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            float c, s;
-            rot_cs<false>(pos_base + r, theta_s[4 * c8 + p], c, s);
-            const float re = x[rr][2 * p], im = x[rr][2 * p + 1];
-            x[rr][2 * p] = re * c - im * s;
-            x[rr][2 * p + 1] = re * s + im * c;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[rr][e] = 0.0f;
+      for (int r = 0; r < TPT; ++r) {
+        const int t = TPT * tg + r;
+        raw[i][r] = (idx < ITEMS && t < valid) ? *(const uint4 *)(src + (long long)t * stride + 8 * c8)
+                                                : make_uint4(0u, 0u, 0u, 0u);
       }
-    }
-    if constexpr (ROWS) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        uint4 o;
-        o.x = pack_bf2(x[rr][0], x[rr][1]);
-        o.y = pack_bf2(x[rr][2], x[rr][3]);
-        o.z = pack_bf2(x[rr][4], x[rr][5]);
-        o.w = pack_bf2(x[rr][6], x[rr][7]);
-        *(uint4 *)(dst + (4 * kq + rr) * (D + 8) + 8 * c8) = o;
-        if constexpr (LO) {
-          // x - bf16(x), rounded to bf16: hi + lo carries ~16 significant bits
-          const uint32_t hw[4] = {o.x, o.y, o.z, o.w};
-          uint4 lo;
-          uint32_t lw[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            lw[e] = pack_bf2(x[rr][2 * e] - __uint_as_float(hw[e] << 16),
-                             x[rr][2 * e + 1] - __uint_as_float(hw[e] & 0xffff0000u));
-          lo.x = lw[0]; lo.y = lw[1]; lo.z = lw[2]; lo.w = lw[3];
-          *(uint4 *)(dstLo + (4 * kq + rr) * (D + 8) + 8 * c8) = lo;
-        }
-      }
-    }
-    if constexpr (TRANS) {
-      float z[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) z[rr] = zeta ? zeta[4 * kq + rr] : 1.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *(u32x2 *)(dstT + (8 * c8 + e) * LDT + 4 * kq) =
-            pack4(x[0][e] * z[0], x[1][e] * z[1], x[2][e] * z[2], x[3][e] * z[3]);
     }
   }
-}
+
+  // rows:  dst[t * ldr + col]            (token-major, bf16; lo part to dstLo when LO)
+  // trans: dstT[col * LDT + t] * zeta_t  (token-minor), zeta_t = gamma^(zoff - t) when `zeta`
+  // Rotation (rot): token t of the tile sits at absolute position p0 + t.
+  template <bool ROWS, bool TRANS, bool LO>
+  __device__ __forceinline__ void commit(bool rot, long long p0, const float *theta_s, const float *rev_s,
+                                         uint16_t *dst, int ldr, uint16_t *dstLo, uint16_t *dstT, bool zeta,
+                                         float zlg, int zoff) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      if (idx >= ITEMS) continue;
+      int tg, c8;
+      item(idx, tg, c8);
+      float x[TPT][8];
+#pragma unroll
+      for (int r = 0; r < TPT; ++r) {
+        const uint32_t wv[4] = {raw[i][r].x, raw[i][r].y, raw[i][r].z, raw[i][r].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[r][2 * e] = __uint_as_float(wv[e] << 16);
+          x[r][2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+        }
+      }
+      if (rot) {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const int pi = 4 * c8 + pp;
+          const float A = base_rev(p0 + TPT * tg, theta_s[pi]);
+          const float w = rev_s[pi];
+#pragma unroll
+          for (int r = 0; r < TPT; ++r) {
+            float rv = __builtin_fmaf((float)r, w, A);
+            rv -= rintf(rv);
+            const float sn = __builtin_amdgcn_sinf(rv), c = __builtin_amdgcn_cosf(rv);
+            const float re = x[r][2 * pp], im = x[r][2 * pp + 1];
+            x[r][2 * pp] = re * c - im * sn;
+            x[r][2 * pp + 1] = re * sn + im * c;
+          }
+        }
+      }
+      if constexpr (ROWS) {
+#pragma unroll
+        for (int r = 0; r < TPT; ++r) {
+          uint4 o;
+          o.x = pack_bf2(x[r][0], x[r][1]);
+          o.y = pack_bf2(x[r][2], x[r][3]);
+          o.z = pack_bf2(x[r][4], x[r][5]);
+          o.w = pack_bf2(x[r][6], x[r][7]);
+          uint16_t *dr = dst + (TPT * tg + r) * ldr + 8 * c8;
+          *(u32x2 *)dr = u32x2{o.x, o.y};
+          *(u32x2 *)(dr + 4) = u32x2{o.z, o.w};
+          if constexpr (LO) {
+            // x - bf16(x), rounded to bf16: hi + lo carries ~16 significant bits
+            const uint32_t hw[4] = {o.x, o.y, o.z, o.w};
+            uint32_t lw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              lw[e] = pack_bf2(x[r][2 * e] - __uint_as_float(hw[e] << 16),
+                               x[r][2 * e + 1] - __uint_as_float(hw[e] & 0xffff0000u));
+            uint16_t *dl = dstLo + (TPT * tg + r) * ldr + 8 * c8;
+            *(u32x2 *)dl = u32x2{lw[0], lw[1]};
+            *(u32x2 *)(dl + 4) = u32x2{lw[2], lw[3]};
+          }
+        }
+      }
+      if constexpr (TRANS) {
+        float z[TPT];
+#pragma unroll
+        for (int r = 0; r < TPT; ++r) {
+          const int d = zoff - (TPT * tg + r);  // d < 0: a zero-filled token past the chunk
+          z[r] = zeta ? (d >= 0 ? dpow(zlg, d) : 0.0f) : 1.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint16_t *row = dstT + (8 * c8 + e) * LDT + TPT * tg;
+          if constexpr (TPT == 2) {
+            *(uint32_t *)row = pack_bf2(x[0][e] * z[0], x[1][e] * z[1]);
+          } else if constexpr (TPT == 4) {
+            *(u32x2 *)row = pack4(x[0][e] * z[0], x[1][e] * z[1], x[2][e] * z[2], x[3][e] * z[3]);
+          } else {
+            *(u32x2 *)row = pack4(x[0][e] * z[0], x[1][e] * z[1], x[2][e] * z[2], x[3][e] * z[3]);
+            *(u32x2 *)(row + 4) = pack4(x[4][e] * z[4], x[5][e] * z[5], x[6][e] * z[6], x[7][e] * z[7]);
+          }
+        }
+      }
+    }
+  }
+
+  // Transposed copy without arithmetic (V tiles): 16-bit halves regrouped with
+  // byte permutes, dstT[col * LDT + t].
+  __device__ __forceinline__ void commit_trans(uint16_t *dstT) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      if (idx >= ITEMS) continue;
+      int tg, c8;
+      item(idx, tg, c8);
+      uint32_t wv[TPT][4];
+#pragma unroll
+      for (int r = 0; r < TPT; ++r) {
+        wv[r][0] = raw[i][r].x;
+        wv[r][1] = raw[i][r].y;
+        wv[r][2] = raw[i][r].z;
+        wv[r][3] = raw[i][r].w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // column e of tokens r, r+1: low halves (e even) or high halves (e odd)
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t pk[TPT / 2];
+#pragma unroll
+        for (int r = 0; r < TPT; r += 2) pk[r / 2] = __builtin_amdgcn_perm(wv[r + 1][e >> 1], wv[r][e >> 1], sel);
+        uint16_t *row = dstT + (8 * c8 + e) * LDT + TPT * tg;
+        if constexpr (TPT == 2) {
+          *(uint32_t *)row = pk[0];
+        } else if constexpr (TPT == 4) {
+          *(u32x2 *)row = u32x2{pk[0], pk[1]};
+        } else {
+          *(u32x2 *)row = u32x2{pk[0], pk[1]};
+          *(u32x2 *)(row + 4) = u32x2{pk[2], pk[3]};
+        }
+      }
+    }
+  }
+};
 
 struct TaskGeom {
   int nseg, seg_chunks, nsplit, nqb, ntasks;
+  int nchunks;  // chunks per (b, h)
 };
 
 // XCD-aware task order: workgroup ids are dealt round-robin to the 8 XCDs, so
@@ -171,188 +298,423 @@ __device__ __forceinline__ int xcd_task(int bid, int ntasks) {
 
 static inline unsigned xcd_grid(int ntasks) { return (unsigned)(((ntasks + 7) / 8) * 8); }
 
-// ---------------------------------------------------------------- main tile kernel
-// PAR: parallel form, one task = (b, h, 64-query block).  Otherwise chunkwise
-// output pass, one task = (b, h, segment, dv slice), state from `seg_state`.
+// Epilogue of a 64-query block held as O^T accumulators: optional GroupNorm over
+// all DV values of each (token, head) row (every wave holds RW of them), optional
+// bf16 gate multiply, store (bf16 or fp32) with the output strides of `a`.
+template <int RB, int RW, int DV>
+__device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB][4], float (*red)[BT], int b, int h,
+                                               int q0, int nvalid, long long obase, int w, int g, int l16) {
+  if (a.use_gn) {
+    float mean[4], inv[4];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      float part[4];
+#pragma unroll
+      for (int qb4 = 0; qb4 < 4; ++qb4) {
+        float sacc = 0.0f;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = ot[rb][qb4][i];
+            sacc += pass == 0 ? x : (x - mean[qb4]) * (x - mean[qb4]);
+          }
+        sacc += __shfl_xor(sacc, 16, 64);
+        sacc += __shfl_xor(sacc, 32, 64);
+        part[qb4] = sacc;
+      }
+      __syncthreads();
+      if (g == 0)
+#pragma unroll
+        for (int qb4 = 0; qb4 < 4; ++qb4) red[w][16 * qb4 + l16] = part[qb4];
+      __syncthreads();
+#pragma unroll
+      for (int qb4 = 0; qb4 < 4; ++qb4) {
+        float tot = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) tot += red[ww][16 * qb4 + l16];
+        tot /= (float)DV;
+        if (pass == 0)
+          mean[qb4] = tot;
+        else
+          inv[qb4] = __builtin_amdgcn_rsqf(tot + a.gn_eps);
+      }
+    }
+#pragma unroll
+    for (int qb4 = 0; qb4 < 4; ++qb4)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = (ot[rb][qb4] - mean[qb4]) * inv[qb4];
+  }
+#pragma unroll
+  for (int qb4 = 0; qb4 < 4; ++qb4) {
+    const int r = 16 * qb4 + l16;
+    if (r < nvalid) {
+      const long long ro = obase + (long long)(q0 + r) * a.o_sn;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int col = w * RW + 16 * rb + 4 * g;
+        f32x4 x = ot[rb][qb4];
+        if (a.gate) {
+          const long long go = (long long)b * a.g_sb + (long long)h * a.g_sh + (long long)(q0 + r) * a.g_sn + col;
+          const u32x2 gg = *(const u32x2 *)(a.gate + go);
+          x[0] *= __uint_as_float(gg.x << 16);
+          x[1] *= __uint_as_float(gg.x & 0xffff0000u);
+          x[2] *= __uint_as_float(gg.y << 16);
+          x[3] *= __uint_as_float(gg.y & 0xffff0000u);
+        }
+        if (a.out_bf16)
+          *(u32x2 *)((uint16_t *)a.o + ro + col) = pack4(x[0], x[1], x[2], x[3]);
+        else
+          *(float4 *)((float *)a.o + ro + col) = make_float4(x[0], x[1], x[2], x[3]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- query-block kernel
+// One task = (b, h, chunk c, 64-query block qb).  PAR: the parallel form (one
+// chunk spanning the sequence, no cross term).  Otherwise the chunkwise output
+// with the incoming state S_c = gamma^(c0-s0) S_in(segment) + local(c), both
+// stored bf16 as S^T[dv][dk] (SinT per segment, locT per chunk).
 // SPLIT: scores from hi + lo bf16 parts of the rotated q and k (three MFMAs per
 // k-step), accurate to ~2^-16 instead of the ~2^-8 of one bf16 rounding of the
 // rotated values.  Used when GroupNorm follows: rows whose variance is near eps
 // magnify absolute score errors by ~1/sqrt(eps).
-template <int DK, int DVW, bool PAR, bool SPLIT>
-__global__ __launch_bounds__(NT) void tile_kernel(RetArgs a, TaskGeom geo, const float *seg_state) {
-  using T = Tile<DK, DVW>;
-  constexpr int LDQ = T::LDQ, RW = T::RW, RB = T::RB, KS = T::KS, DKB = T::DKB;
-  // Chunkwise: Qs (rotated query block, bf16) is read only before the key loop and
-  // Kt only inside it, so they share storage.  Parallel: the query block is staged
-  // through Ks / KsL, which are free until the key loop starts.
-  constexpr int QK_SZ = PAR ? 8 : (BT * LDQ > DK * LDT ? BT * LDQ : DK * LDT);
-  __shared__ __attribute__((aligned(16))) uint16_t QKs[QK_SZ];
+// The global loads of the next key block are issued right after the current
+// one is committed to LDS, so they are in flight during the MFMA work.
+template <int DK, int DV, bool PAR, bool SPLIT>
+__global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, const uint16_t *SinT,
+                                                    const uint16_t *locT) {
+  using T = Tile<DK, DV>;
+  constexpr int LDQ = T::LDQ, RW = T::RW, RB = T::RB, KS = T::KS;
+  // The query block is staged through Ks / KsL (free until the key loop starts).
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BT * LDQ];
   __shared__ __attribute__((aligned(16))) uint16_t KsL[SPLIT ? BT * LDQ : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DVW * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * LDT];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[BT * LDT];
-  uint16_t *const Qs = PAR ? Ks : QKs;
-  uint16_t *const Kt = QKs;
-  __shared__ float theta_s[DK / 2];
-  __shared__ float zeta_s[BT];
+  __shared__ float theta_s[DK / 2], rev_s[DK / 2];
   __shared__ float red[8][BT];
+  __shared__ float dt[DT_SZ];
+  uint16_t *const Qs = Ks;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int task = xcd_task(blockIdx.x, geo.ntasks);
   if (task < 0) return;
-
-  int bh, split = 0, seg = 0, qb_only = 0;
-  if constexpr (PAR) {
-    bh = task / geo.nqb;
-    qb_only = geo.nqb - 1 - task % geo.nqb;  // longest blocks first
-  } else {
-    split = task % geo.nsplit;
-    seg = (task / geo.nsplit) % geo.nseg;
-    bh = task / (geo.nsplit * geo.nseg);
-  }
+  // task order: (bh, chunk, qb) with qb fastest; longest query blocks first
+  const int qb = geo.nqb - 1 - task % geo.nqb;
+  const int c = (task / geo.nqb) % geo.nchunks;
+  const int bh = task / (geo.nqb * geo.nchunks);
+  const int cstep = PAR ? a.L : a.chunk;
+  const int c0 = c * cstep, Cc = min(cstep, a.L - c0);
+  const int q0 = c0 + qb * BT;
+  if (q0 >= c0 + Cc) return;  // short last chunk: fewer query blocks
   const int b = bh / a.H, h = bh % a.H;
   const float lg = safe_log2(a.gamma[h]);
+  const bool rot = a.use_theta;
   const uint16_t *q = (const uint16_t *)a.q + (long long)b * a.q_sb + (long long)h * a.q_sh;
   const uint16_t *k = (const uint16_t *)a.k + (long long)b * a.q_sb + (long long)h * a.q_sh;
-  const uint16_t *v = (const uint16_t *)a.v + (long long)b * a.v_sb + (long long)h * a.v_sh + split * DVW;
-  const long long obase = (long long)b * a.o_sb + (long long)h * a.o_sh + split * DVW;
-  if (a.use_theta)
-    for (int i = tid; i < DK / 2; i += NT) theta_s[i] = a.theta[i];
+  const uint16_t *v = (const uint16_t *)a.v + (long long)b * a.v_sb + (long long)h * a.v_sh;
+  const long long obase = (long long)b * a.o_sb + (long long)h * a.o_sh;
+  if (rot)
+    for (int i = tid; i < DK / 2; i += NT) {
+      theta_s[i] = a.theta[i];
+      rev_s[i] = (float)((double)a.theta[i] * 0.15915494309189535);
+    }
+  fill_decay_table(dt, lg, NT);
 
-  // fp32 state S[dk][w*RW + dv'] in D layout: st[dkb][rb][i] = S[16dkb+4g+i][w*RW+16rb+l16]
-  f32x4 st[PAR ? 1 : DKB][PAR ? 1 : RB];
-  int t_lo, t_hi;  // token range of the task
-  if constexpr (PAR) {
-    t_lo = 0;
-    t_hi = a.L;
-  } else {
-    const int c_lo = seg * geo.seg_chunks;
-    t_lo = c_lo * a.chunk;
-    t_hi = min(a.L, (c_lo + geo.seg_chunks) * a.chunk);
-    const float *S_in = seg_state + ((long long)bh * geo.nseg + seg) * DK * a.dv + split * DVW;
+  TileIO<DK> qio, kio;
+  TileIO<DV> vio;
+  qio.fetch(q + (long long)q0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - q0));
+  kio.fetch(k + (long long)c0 * a.q_sn, a.q_sn, min(BT, Cc));
+  vio.fetch(v + (long long)c0 * a.v_sn, a.v_sn, min(BT, Cc));
+  __syncthreads();
+  qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, rev_s, Qs, LDQ, KsL, nullptr, false, 0.f, 0);
+  __syncthreads();
+  const int qblk = w & 3, kh = w >> 2;  // score split: 16 queries x 32 keys per wave
+  u32x4 qreg[KS], qlo[SPLIT ? KS : 1];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qreg[ks] = ld_op(Qs + (16 * qblk + l16) * LDQ, 32 * ks, g);
+    if constexpr (SPLIT) qlo[ks] = ld_op(KsL + (16 * qblk + l16) * LDQ, 32 * ks, g);
+  }
+  // O^T accumulators: ot[rb][qb4][i] = O^T[w*RW+16rb+4g+i][16qb4+l16]
+  f32x4 ot[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int qb4 = 0; qb4 < 4; ++qb4) ot[rb][qb4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (!PAR) {
+    // cross term gamma^(j+1) q S_c.  A operand rows: S_c^T[w*RW + 16rb + l16][dk K-set]
+    const int seg = c / geo.seg_chunks;
+    const int s0 = seg * geo.seg_chunks * a.chunk;
+    const bool has_loc = c % geo.seg_chunks != 0;
+    const float gs = dpow(lg, c0 - s0);
+    const uint16_t *sin_t = SinT + ((long long)bh * geo.nseg + seg) * DK * DV;
+    const uint16_t *loc_t = locT + ((long long)bh * geo.nchunks + c) * DK * DV;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 as[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const long long off = (long long)(w * RW + 16 * rb + l16) * DK + 32 * ks + 4 * g;
+        const u32x2 s_lo = *(const u32x2 *)(sin_t + off), s_hi = *(const u32x2 *)(sin_t + off + 16);
+        const uint32_t sw[4] = {s_lo.x, s_lo.y, s_hi.x, s_hi.y};
+        uint32_t aw[4];
+        if (has_loc) {
+          const u32x2 l_lo = *(const u32x2 *)(loc_t + off), l_hi = *(const u32x2 *)(loc_t + off + 16);
+          const uint32_t lw[4] = {l_lo.x, l_lo.y, l_hi.x, l_hi.y};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            aw[e] = pack_bf2(__builtin_fmaf(gs, __uint_as_float(sw[e] << 16), __uint_as_float(lw[e] << 16)),
+                             __builtin_fmaf(gs, __uint_as_float(sw[e] & 0xffff0000u),
+                                            __uint_as_float(lw[e] & 0xffff0000u)));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            aw[e] = pack_bf2(gs * __uint_as_float(sw[e] << 16), gs * __uint_as_float(sw[e] & 0xffff0000u));
+        }
+        as[rb] = u32x4{aw[0], aw[1], aw[2], aw[3]};
+      }
+#pragma unroll
+      for (int qb4 = 0; qb4 < 4; ++qb4) {
+        const u32x4 bq = ld_op(Qs + (16 * qb4 + l16) * LDQ, 32 * ks, g);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = mfma(as[rb], bq, ot[rb][qb4]);
+      }
+    }
+#pragma unroll
+    for (int qb4 = 0; qb4 < 4; ++qb4) {
+      const float xi = dpow(lg, q0 - c0 + 16 * qb4 + l16 + 1);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] *= xi;
+    }
+  }
+  for (int kb = 0; kb <= qb; ++kb) {
+    const int k0 = c0 + kb * BT;
+    const int delta = qb - kb;
+    const float gdel = delta ? dpow(lg, 64 * (delta - 1)) : 1.0f;
+    __syncthreads();
+    kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Ks, LDQ, KsL, nullptr, false, 0.f, 0);
+    vio.commit_trans(Vt);
+    __syncthreads();
+    if (kb < qb) {
+      const int n0 = k0 + BT;
+      kio.fetch(k + (long long)n0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - n0));
+      vio.fetch(v + (long long)n0 * a.v_sn, a.v_sn, min(BT, c0 + Cc - n0));
+    }
+    // scores S^T[key][query] for keys 32kh..+32, queries 16qblk..+16; decay, mask, -> Ps
+#pragma unroll
+    for (int kb16 = 0; kb16 < 2; ++kb16) {
+      f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 ak = ld_op(Ks + (32 * kh + 16 * kb16 + l16) * LDQ, 32 * ks, g);
+        sc = mfma(ak, qreg[ks], sc);
+        if constexpr (SPLIT) {
+          sc = mfma(ld_op(KsL + (32 * kh + 16 * kb16 + l16) * LDQ, 32 * ks, g), qreg[ks], sc);
+          sc = mfma(ak, qlo[ks], sc);
+        }
+      }
+      // decay and causal mask from the table (delta = qb - kb blocks apart)
+      const int dp = (16 * qblk + l16) - (32 * kh + 16 * kb16 + 4 * g) + (delta ? 128 : 64);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = sc[i] * (gdel * dt[dp - i]);
+      *(u32x2 *)(Ps + (16 * qblk + l16) * LDT + 32 * kh + 16 * kb16 + 4 * g) = pack4(p[0], p[1], p[2], p[3]);
+    }
+    __syncthreads();
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 av[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) av[rb] = ld_op(Vt + (w * RW + 16 * rb + l16) * LDT, 32 * ks, g);
+#pragma unroll
+      for (int qb4 = 0; qb4 < 4; ++qb4) {
+        const u32x4 bp = ld_op(Ps + (16 * qb4 + l16) * LDT, 32 * ks, g);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = mfma(av[rb], bp, ot[rb][qb4]);
+      }
+    }
+  }
+  epilogue_store<RB, RW, DV>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
+}
+
+// ---------------------------------------------------------------- segment output kernel
+// Chunkwise output when the fp32 state of one (b, h), DK x DV, fits in the
+// accumulators of the 8 waves (DK*DV <= 128*256).  One task = (b, h, segment):
+// the state S_in(segment) is loaded once, then for every chunk of the segment
+// and every 64-query block qb of the chunk: the cross term gamma^(j+1) q S_c
+// (A operand = S_c^T in bf16, straight from the accumulators: D blocks (2ks, rb)
+// and (2ks+1, rb) are the two halves of k-step ks), then the key blocks
+// kb = 0..qb.  The chunk's key blocks are folded into the state only while the
+// last query block runs (it visits them all), so the cross terms of the
+// earlier blocks see S_c.  Global loads of the next visit are in flight
+// during the current one.
+template <int DK, int DV, bool SPLIT>
+__global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, const float *seg_state) {
+  using T = Tile<DK, DV>;
+  constexpr int LDQ = T::LDQ, RW = T::RW, RB = T::RB, KS = T::KS, DKB = T::DKB;
+  // Qs (rotated query block, bf16) is read only before the key loop and Kt
+  // (zeta-scaled transposed keys of the update) only inside it: shared storage.
+  constexpr int QK_SZ = BT * LDQ > DK * LDT ? BT * LDQ : DK * LDT;
+  __shared__ __attribute__((aligned(16))) uint16_t QKs[QK_SZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BT * LDQ];
+  __shared__ __attribute__((aligned(16))) uint16_t KsL[SPLIT ? BT * LDQ : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[BT * LDT];
+  uint16_t *const Qs = QKs;
+  uint16_t *const Kt = QKs;
+  __shared__ float theta_s[DK / 2], rev_s[DK / 2];
+  __shared__ float red[8][BT];
+  __shared__ float dt[DT_SZ];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int task = xcd_task(blockIdx.x, geo.ntasks);
+  if (task < 0) return;
+  const int seg = task % geo.nseg;
+  const int bh = task / geo.nseg;
+  const int b = bh / a.H, h = bh % a.H;
+  const float lg = safe_log2(a.gamma[h]);
+  const bool rot = a.use_theta;
+  const uint16_t *q = (const uint16_t *)a.q + (long long)b * a.q_sb + (long long)h * a.q_sh;
+  const uint16_t *k = (const uint16_t *)a.k + (long long)b * a.q_sb + (long long)h * a.q_sh;
+  const uint16_t *v = (const uint16_t *)a.v + (long long)b * a.v_sb + (long long)h * a.v_sh;
+  const long long obase = (long long)b * a.o_sb + (long long)h * a.o_sh;
+  if (rot)
+    for (int i = tid; i < DK / 2; i += NT) {
+      theta_s[i] = a.theta[i];
+      rev_s[i] = (float)((double)a.theta[i] * 0.15915494309189535);
+    }
+  fill_decay_table(dt, lg, NT);
+
+  // fp32 state in D layout: st[dkb][rb][i] = S[16dkb+4g+i][w*RW+16rb+l16]
+  f32x4 st[DKB][RB];
+  const int c_lo = seg * geo.seg_chunks;
+  const int t_lo = c_lo * a.chunk;
+  const int t_hi = min(a.L, (c_lo + geo.seg_chunks) * a.chunk);
+  {
+    const float *S_in = seg_state + ((long long)bh * geo.nseg + seg) * DK * DV;
 #pragma unroll
     for (int dkb = 0; dkb < DKB; ++dkb)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          st[dkb][rb][i] = S_in[(long long)(16 * dkb + 4 * g + i) * a.dv + w * RW + 16 * rb + l16];
+          st[dkb][rb][i] = S_in[(long long)(16 * dkb + 4 * g + i) * DV + w * RW + 16 * rb + l16];
   }
-  __syncthreads();
+  TileIO<DK> qio, kio;
+  TileIO<DV> vio;
+  {
+    const int Cc = min(a.chunk, a.L - t_lo);
+    qio.fetch(q + (long long)t_lo * a.q_sn, a.q_sn, min(BT, Cc));
+    kio.fetch(k + (long long)t_lo * a.q_sn, a.q_sn, min(BT, Cc));
+    vio.fetch(v + (long long)t_lo * a.v_sn, a.v_sn, min(BT, Cc));
+  }
 
   const int qblk = w & 3, kh = w >> 2;  // score split: 16 queries x 32 keys per wave
-  for (int c0 = t_lo; c0 < t_hi; c0 += (PAR ? a.L : a.chunk)) {
-    const int Cc = PAR ? a.L : min(a.chunk, a.L - c0);
-    const bool carry = !PAR && (c0 + Cc < t_hi);  // state needed after this chunk
+  for (int c0 = t_lo; c0 < t_hi; c0 += a.chunk) {
+    const int Cc = min(a.chunk, a.L - c0);
+    const bool carry = c0 + Cc < t_hi;  // state needed after this chunk
     const int nqb_c = (Cc + BT - 1) / BT;
-    for (int qb = (PAR ? qb_only : 0); qb < (PAR ? qb_only + 1 : nqb_c); ++qb) {
-      const int q0 = c0 + qb * BT;  // first query of the block
+    for (int qb = 0; qb < nqb_c; ++qb) {
+      const int q0 = c0 + qb * BT;
+      const bool last_qb = qb == nqb_c - 1;
       __syncthreads();
-      if (a.use_theta)
-        stage<DK, true, false, true, SPLIT>(q + (long long)q0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - q0),
-                                            a.pos0 + q0, theta_s, Qs, nullptr, nullptr, KsL);
-      else
-        stage<DK, true, false, false, SPLIT>(q + (long long)q0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - q0), 0,
-                                             theta_s, Qs, nullptr, nullptr, KsL);
+      qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, rev_s, Qs, LDQ, KsL, nullptr, false, 0.f,
+                                              0);
       __syncthreads();
-      // this wave's query operand for the scores (hi, and lo when SPLIT)
       u32x4 qreg[KS], qlo[SPLIT ? KS : 1];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         qreg[ks] = ld_op(Qs + (16 * qblk + l16) * LDQ, 32 * ks, g);
         if constexpr (SPLIT) qlo[ks] = ld_op(KsL + (16 * qblk + l16) * LDQ, 32 * ks, g);
       }
-      // O^T accumulators: ot[rb][qb4][i] = O^T[w*RW+16rb+4g+i][16qb4+l16]
       f32x4 ot[RB][4];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int qb4 = 0; qb4 < 4; ++qb4) ot[rb][qb4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      // The state still holds S_c here: the chunk's key blocks are folded into it
-      // only while the last query block of the chunk runs (it visits them all).
-      const bool last_qb = qb == nqb_c - 1;
-      if constexpr (!PAR) {
-        // cross term gamma^(j+1) q S_c; A operand = S_c^T in bf16, straight from the
-        // accumulators: D blocks (2ks, rb) and (2ks+1, rb) are the two halves of k-step ks
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          u32x4 as[RB];
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 as[RB];
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const f32x4 lo = st[2 * ks][rb], hi = st[2 * ks + 1][rb];
-            as[rb] = u32x4{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(hi[0], hi[1]),
-                           pack_bf2(hi[2], hi[3])};
-          }
-#pragma unroll
-          for (int qb4 = 0; qb4 < 4; ++qb4) {
-            const u32x4 bq = ld_op(Qs + (16 * qb4 + l16) * LDQ, 32 * ks, g);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = mfma(as[rb], bq, ot[rb][qb4]);
-          }
+        for (int rb = 0; rb < RB; ++rb) {
+          const f32x4 lo = st[2 * ks][rb], hi = st[2 * ks + 1][rb];
+          as[rb] = u32x4{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
         }
 #pragma unroll
         for (int qb4 = 0; qb4 < 4; ++qb4) {
-          const float xi = dpow(lg, q0 - c0 + 16 * qb4 + l16 + 1);
+          const u32x4 bq = ld_op(Qs + (16 * qb4 + l16) * LDQ, 32 * ks, g);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] *= xi;
+          for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = mfma(as[rb], bq, ot[rb][qb4]);
         }
-        if (carry && last_qb) {
-          const float gc = dpow(lg, Cc);
+      }
 #pragma unroll
-          for (int dkb = 0; dkb < DKB; ++dkb)
+      for (int qb4 = 0; qb4 < 4; ++qb4) {
+        const float xi = dpow(lg, q0 - c0 + 16 * qb4 + l16 + 1);
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) st[dkb][rb] *= gc;
-        }
+        for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] *= xi;
+      }
+      if (carry && last_qb) {
+        const float gc = dpow(lg, Cc);
+#pragma unroll
+        for (int dkb = 0; dkb < DKB; ++dkb)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) st[dkb][rb] *= gc;
       }
       for (int kb = 0; kb <= qb; ++kb) {
         const int k0 = c0 + kb * BT;
-        const int kvalid = min(BT, c0 + Cc - k0);
         const bool upd = carry && last_qb;
+        const int delta = qb - kb;
+        const float gdel = delta ? dpow(lg, 64 * (delta - 1)) : 1.0f;
         __syncthreads();
         if (upd)
-          for (int r = tid; r < BT; r += NT) zeta_s[r] = r < kvalid ? dpow(lg, Cc - 1 - (k0 - c0 + r)) : 0.0f;
+          kio.template commit<true, true, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Ks, LDQ, KsL, Kt, true, lg,
+                                                 Cc - 1 - (k0 - c0));
+        else
+          kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Ks, LDQ, KsL, nullptr, false, 0.f,
+                                                  0);
+        vio.commit_trans(Vt);
         __syncthreads();
-        const uint16_t *kp = k + (long long)k0 * a.q_sn;
-        if (a.use_theta) {
-          if (upd)
-            stage<DK, true, true, true, SPLIT>(kp, a.q_sn, kvalid, a.pos0 + k0, theta_s, Ks, Kt, zeta_s, KsL);
-          else
-            stage<DK, true, false, true, SPLIT>(kp, a.q_sn, kvalid, a.pos0 + k0, theta_s, Ks, nullptr, nullptr,
-                                                KsL);
+        // prefetch the next visit: next key block of this query block, else the
+        // next query block (of this chunk, or the first of the next chunk)
+        if (kb < qb) {
+          const int n0 = k0 + BT;
+          kio.fetch(k + (long long)n0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - n0));
+          vio.fetch(v + (long long)n0 * a.v_sn, a.v_sn, min(BT, c0 + Cc - n0));
         } else {
-          if (upd)
-            stage<DK, true, true, false, SPLIT>(kp, a.q_sn, kvalid, 0, theta_s, Ks, Kt, zeta_s, KsL);
-          else
-            stage<DK, true, false, false, SPLIT>(kp, a.q_sn, kvalid, 0, theta_s, Ks, nullptr, nullptr, KsL);
+          int nc0 = c0, nq0 = q0 + BT;
+          if (qb + 1 >= nqb_c) {
+            nc0 = c0 + Cc;
+            nq0 = nc0;
+          }
+          if (nc0 < t_hi) {
+            const int nCc = min(a.chunk, a.L - nc0);
+            qio.fetch(q + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nc0 + nCc - nq0));
+            kio.fetch(k + (long long)nc0 * a.q_sn, a.q_sn, min(BT, nCc));
+            vio.fetch(v + (long long)nc0 * a.v_sn, a.v_sn, min(BT, nCc));
+          }
         }
-        stage<DVW, false, true, false>(v + (long long)k0 * a.v_sn, a.v_sn, kvalid, 0, theta_s, nullptr, Vt,
-                                       nullptr);
-        __syncthreads();
-        // scores S^T[key][query] for keys 32kh..+32, queries 16qblk..+16; decay, mask, -> Ps
 #pragma unroll
         for (int kb16 = 0; kb16 < 2; ++kb16) {
-          f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+          f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const u32x4 ak = ld_op(Ks + (32 * kh + 16 * kb16 + l16) * LDQ, 32 * ks, g);
-            s = mfma(ak, qreg[ks], s);
+            sc = mfma(ak, qreg[ks], sc);
             if constexpr (SPLIT) {
-              s = mfma(ld_op(KsL + (32 * kh + 16 * kb16 + l16) * LDQ, 32 * ks, g), qreg[ks], s);
-              s = mfma(ak, qlo[ks], s);
+              sc = mfma(ld_op(KsL + (32 * kh + 16 * kb16 + l16) * LDQ, 32 * ks, g), qreg[ks], sc);
+              sc = mfma(ak, qlo[ks], sc);
             }
           }
-          const int n = q0 + 16 * qblk + l16;
-          const int m0 = k0 + 32 * kh + 16 * kb16 + 4 * g;
+          const int dp = (16 * qblk + l16) - (32 * kh + 16 * kb16 + 4 * g) + (delta ? 128 : 64);
           float p[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d = n - (m0 + i);
-            p[i] = d >= 0 ? s[i] * dpow(lg, d) : 0.0f;
-          }
+          for (int i = 0; i < 4; ++i) p[i] = sc[i] * (gdel * dt[dp - i]);
           *(u32x2 *)(Ps + (16 * qblk + l16) * LDT + 32 * kh + 16 * kb16 + 4 * g) = pack4(p[0], p[1], p[2], p[3]);
         }
         __syncthreads();
-        // O^T += V^T P^T
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           u32x4 av[RB];
@@ -364,97 +726,36 @@ __global__ __launch_bounds__(NT) void tile_kernel(RetArgs a, TaskGeom geo, const
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = mfma(av[rb], bp, ot[rb][qb4]);
           }
-        }
-        if constexpr (!PAR) {
           if (upd) {
             // S += (zeta K)^T V over this key block
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              u32x4 bv[RB];
+            for (int dkb = 0; dkb < DKB; ++dkb) {
+              const u32x4 ak = ld_op(Kt + (16 * dkb + l16) * LDT, 32 * ks, g);
 #pragma unroll
-              for (int rb = 0; rb < RB; ++rb) bv[rb] = ld_op(Vt + (w * RW + 16 * rb + l16) * LDT, 32 * ks, g);
-#pragma unroll
-              for (int dkb = 0; dkb < DKB; ++dkb) {
-                const u32x4 ak = ld_op(Kt + (16 * dkb + l16) * LDT, 32 * ks, g);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = mfma(ak, bv[rb], st[dkb][rb]);
-              }
+              for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = mfma(ak, av[rb], st[dkb][rb]);
             }
           }
         }
       }
-      // ---- epilogue: optional GroupNorm over dv (only when this block holds all of dv), store
-      const int nvalid = min(BT, c0 + Cc - q0);
-      if (a.use_gn && DVW == a.dv) {
-        float mean[4], inv[4];
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-          float part[4];
-#pragma unroll
-          for (int qb4 = 0; qb4 < 4; ++qb4) {
-            float sacc = 0.0f;
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float x = ot[rb][qb4][i];
-                sacc += pass == 0 ? x : (x - mean[qb4]) * (x - mean[qb4]);
-              }
-            sacc += __shfl_xor(sacc, 16, 64);
-            sacc += __shfl_xor(sacc, 32, 64);
-            part[qb4] = sacc;
-          }
-          __syncthreads();
-          if (g == 0)
-#pragma unroll
-            for (int qb4 = 0; qb4 < 4; ++qb4) red[w][16 * qb4 + l16] = part[qb4];
-          __syncthreads();
-#pragma unroll
-          for (int qb4 = 0; qb4 < 4; ++qb4) {
-            float tot = 0.0f;
-#pragma unroll
-            for (int ww = 0; ww < 8; ++ww) tot += red[ww][16 * qb4 + l16];
-            tot /= (float)a.dv;
-            if (pass == 0)
-              mean[qb4] = tot;
-            else
-              inv[qb4] = 1.0f / sqrtf(tot + a.gn_eps);
-          }
-        }
-#pragma unroll
-        for (int qb4 = 0; qb4 < 4; ++qb4)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = (ot[rb][qb4] - mean[qb4]) * inv[qb4];
-      }
-#pragma unroll
-      for (int qb4 = 0; qb4 < 4; ++qb4) {
-        const int r = 16 * qb4 + l16;
-        if (r < nvalid) {
-          const long long ro = obase + (long long)(q0 + r) * a.o_sn;
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const int col = w * RW + 16 * rb + 4 * g;
-            const f32x4 x = ot[rb][qb4];
-            if (a.out_bf16)
-              *(u32x2 *)((uint16_t *)a.o + ro + col) = pack4(x[0], x[1], x[2], x[3]);
-            else
-              *(float4 *)((float *)a.o + ro + col) = make_float4(x[0], x[1], x[2], x[3]);
-          }
-        }
-      }
+      epilogue_store<RB, RW, DV>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
     }
   }
 }
 
 // ---------------------------------------------------------------- pass 1: segment states
+// Walks the segment chunk by chunk from a zero state:
+//   S <- gamma^Cc S + sum_i gamma^(Cc-1-i) k_i^T v_i     (per chunk)
+// 64 tokens at a time, double-buffered in LDS with the next block's global
+// loads in flight.  Before every chunk after the first it stores S (the local
+// state entering that chunk) as bf16 S^T[dv][dk] in locT; at the end it stores
+// the segment's own state (fp32, [dk][dv]) in seg_state.
 template <int DK, int DVW>
-__global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, float *seg_state) {
+__global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, float *seg_state, uint16_t *locT) {
   using T = Tile<DK, DVW>;
   constexpr int RW = T::RW, RB = T::RB, DKB = T::DKB;
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DVW * LDT];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[DK * LDT];
-  __shared__ float theta_s[DK / 2];
-  __shared__ float zeta_s[BT];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DVW * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][DK * LDT];
+  __shared__ float theta_s[DK / 2], rev_s[DK / 2];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int task = xcd_task(blockIdx.x, geo.ntasks);
   if (task < 0) return;
@@ -466,38 +767,72 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
   const uint16_t *k = (const uint16_t *)a.k + (long long)b * a.q_sb + (long long)h * a.q_sh;
   const uint16_t *v = (const uint16_t *)a.v + (long long)b * a.v_sb + (long long)h * a.v_sh + split * DVW;
   if (a.use_theta)
-    for (int i = tid; i < DK / 2; i += NT) theta_s[i] = a.theta[i];
-  const int t_lo = seg * geo.seg_chunks * a.chunk;
-  const int t_hi = min(a.L, (seg + 1) * geo.seg_chunks * a.chunk);
+    for (int i = tid; i < DK / 2; i += NT) {
+      theta_s[i] = a.theta[i];
+      rev_s[i] = (float)((double)a.theta[i] * 0.15915494309189535);
+    }
+  __syncthreads();
+  const int c_lo = seg * geo.seg_chunks;
+  const int c_hi = min(geo.nchunks, c_lo + geo.seg_chunks);
+  const int t_lo = c_lo * a.chunk, t_hi = min(a.L, c_hi * a.chunk);
   f32x4 st[DKB][RB];
 #pragma unroll
   for (int dkb = 0; dkb < DKB; ++dkb)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = t_lo; k0 < t_hi; k0 += BT) {
-    const int kvalid = min(BT, t_hi - k0);
-    __syncthreads();
-    for (int r = tid; r < BT; r += NT) zeta_s[r] = r < kvalid ? dpow(lg, t_hi - 1 - (k0 + r)) : 0.0f;
-    __syncthreads();
-    if (a.use_theta)
-      stage<DK, false, true, true>(k + (long long)k0 * a.q_sn, a.q_sn, kvalid, a.pos0 + k0, theta_s, nullptr,
-                                   Kt, zeta_s);
-    else
-      stage<DK, false, true, false>(k + (long long)k0 * a.q_sn, a.q_sn, kvalid, 0, theta_s, nullptr, Kt,
-                                    zeta_s);
-    stage<DVW, false, true, false>(v + (long long)k0 * a.v_sn, a.v_sn, kvalid, 0, theta_s, nullptr, Vt,
-                                   nullptr);
-    __syncthreads();
+  TileIO<DK> kio;
+  TileIO<DVW> vio;
+  kio.fetch(k + (long long)t_lo * a.q_sn, a.q_sn, min(BT, min(a.chunk, t_hi - t_lo)));
+  vio.fetch(v + (long long)t_lo * a.v_sn, a.v_sn, min(BT, min(a.chunk, t_hi - t_lo)));
+  int buf = 0;
+  for (int c = c_lo; c < c_hi; ++c) {
+    const int c0 = c * a.chunk, Cc = min(a.chunk, a.L - c0);
+    if (c > c_lo) {
+      // local state entering chunk c -> locT (bf16, S^T[dv][dk]) when requested; then
+      // decay it over the chunk
+      if (locT) {
+        uint16_t *dst = locT + ((long long)bh * geo.nchunks + c) * DK * a.dv;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 bv[RB];
+        for (int dkb = 0; dkb < DKB; ++dkb)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) bv[rb] = ld_op(Vt + (w * RW + 16 * rb + l16) * LDT, 32 * ks, g);
+          for (int rb = 0; rb < RB; ++rb)
+            *(u32x2 *)(dst + (long long)(split * DVW + w * RW + 16 * rb + l16) * DK + 16 * dkb + 4 * g) =
+                pack4(st[dkb][rb][0], st[dkb][rb][1], st[dkb][rb][2], st[dkb][rb][3]);
+      }
+      const float gc = dpow(lg, Cc);
 #pragma unroll
-      for (int dkb = 0; dkb < DKB; ++dkb) {
-        const u32x4 ak = ld_op(Kt + (16 * dkb + l16) * LDT, 32 * ks, g);
+      for (int dkb = 0; dkb < DKB; ++dkb)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = mfma(ak, bv[rb], st[dkb][rb]);
+        for (int rb = 0; rb < RB; ++rb) st[dkb][rb] *= gc;
+    }
+    for (int k0 = c0; k0 < c0 + Cc; k0 += BT, buf ^= 1) {
+      // buffer `buf` was last read two blocks ago; the barrier of the previous
+      // block ordered those reads before this write
+      kio.template commit<false, true, false>(a.use_theta, a.pos0 + k0, theta_s, rev_s, nullptr, 0, nullptr, Kt[buf],
+                                              true, lg, c0 + Cc - 1 - k0);
+      vio.commit_trans(Vt[buf]);
+      __syncthreads();
+      // prefetch the next block: this chunk's next, else the next chunk's first
+      int n0 = k0 + BT, nend = c0 + Cc;
+      if (n0 >= nend) {
+        n0 = c0 + Cc;
+        nend = min(a.L, n0 + a.chunk);
+      }
+      if (n0 < t_hi) {
+        kio.fetch(k + (long long)n0 * a.q_sn, a.q_sn, min(BT, nend - n0));
+        vio.fetch(v + (long long)n0 * a.v_sn, a.v_sn, min(BT, nend - n0));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 bv[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) bv[rb] = ld_op(Vt[buf] + (w * RW + 16 * rb + l16) * LDT, 32 * ks, g);
+#pragma unroll
+        for (int dkb = 0; dkb < DKB; ++dkb) {
+          const u32x4 ak = ld_op(Kt[buf] + (16 * dkb + l16) * LDT, 32 * ks, g);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = mfma(ak, bv[rb], st[dkb][rb]);
+        }
       }
     }
   }
@@ -513,9 +848,10 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
 
 // ---------------------------------------------------------------- pass 2: scan over segments
 // In place: ws[bh][s] holds the segment's own state on entry and the state
-// entering segment s on exit.  Also writes the state after the last token.
-__global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, float *ws, const float *state_in,
-                                                       float *state_out) {
+// entering segment s on exit; sinT[bh][s] receives the same as bf16
+// S^T[dv][dk].  Also writes the state after the last token.
+__global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, float *ws, uint16_t *sinT,
+                                                       const float *state_in, float *state_out) {
   const long long SZ = (long long)a.dk * a.dv;
   const long long n4 = SZ / 4;
   const int bh = blockIdx.y;
@@ -525,28 +861,20 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, 
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += (long long)gridDim.x * blockDim.x) {
     float4 run = state_in ? ((const float4 *)(state_in + (long long)bh * SZ))[e] : make_float4(0.f, 0.f, 0.f, 0.f);
     float4 *base = (float4 *)(ws + (long long)bh * geo.nseg * SZ);
-    int s = 0;
-    constexpr int U = 4;
-    for (; s + U <= geo.nseg; s += U) {
-      float4 d[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) d[u] = base[(long long)(s + u) * n4 + e];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        base[(long long)(s + u) * n4 + e] = run;
-        const int len = min(a.L, (s + u + 1) * seg_len) - (s + u) * seg_len;
-        const float gm = len == seg_len ? g_full : dpow(lg, len);
-        run.x = gm * run.x + d[u].x;
-        run.y = gm * run.y + d[u].y;
-        run.z = gm * run.z + d[u].z;
-        run.w = gm * run.w + d[u].w;
-      }
-    }
-    for (; s < geo.nseg; ++s) {
+    uint16_t *tb = sinT ? sinT + (long long)bh * geo.nseg * SZ : nullptr;
+    const int row = (int)(4 * e / a.dv), col = (int)(4 * e % a.dv);  // element (dk row, dv col..col+3)
+    for (int s = 0; s < geo.nseg; ++s) {
       const float4 d = base[(long long)s * n4 + e];
       base[(long long)s * n4 + e] = run;
+      if (sinT) {
+        uint16_t *t = tb + (long long)s * SZ + row;
+        t[(long long)(col + 0) * a.dk] = f2bf(run.x);
+        t[(long long)(col + 1) * a.dk] = f2bf(run.y);
+        t[(long long)(col + 2) * a.dk] = f2bf(run.z);
+        t[(long long)(col + 3) * a.dk] = f2bf(run.w);
+      }
       const int len = min(a.L, (s + 1) * seg_len) - s * seg_len;
-      const float gm = dpow(lg, len);
+      const float gm = len == seg_len ? g_full : dpow(lg, len);
       run.x = gm * run.x + d.x;
       run.y = gm * run.y + d.y;
       run.z = gm * run.z + d.z;
@@ -556,46 +884,15 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, 
   }
 }
 
-// GroupNorm of output rows in place, for chunkwise launches whose dv is split
-// over several workgroups.  One block per (b, h, token) row.
-__global__ __launch_bounds__(256) void gn_rows_kernel(RetArgs a) {
-  __shared__ float red[4];
-  const long long row = blockIdx.x;
-  const int n = (int)(row % a.L);
-  const int bh = (int)(row / a.L);
-  const long long off = (long long)(bh / a.H) * a.o_sb + (long long)(bh % a.H) * a.o_sh + (long long)n * a.o_sn;
-  float x[RETENTION_MAX_DV / 256];
-  float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < RETENTION_MAX_DV / 256; ++c) {
-    const int j = threadIdx.x + 256 * c;
-    x[c] = j < a.dv ? load_elem(a.o, off + j, a.out_bf16) : 0.0f;
-    s += x[c];
-  }
-  const float mean = block_sum<256>(s, red) / (float)a.dv;
-  float q = 0.0f;
-#pragma unroll
-  for (int c = 0; c < RETENTION_MAX_DV / 256; ++c) {
-    const int j = threadIdx.x + 256 * c;
-    if (j < a.dv) q += (x[c] - mean) * (x[c] - mean);
-  }
-  const float inv = 1.0f / sqrtf(block_sum<256>(q, red) / (float)a.dv + a.gn_eps);
-#pragma unroll
-  for (int c = 0; c < RETENTION_MAX_DV / 256; ++c) {
-    const int j = threadIdx.x + 256 * c;
-    if (j < a.dv) store_elem(a.o, off + j, (x[c] - mean) * inv, a.out_bf16);
-  }
-}
-
 // ---------------------------------------------------------------- dispatch
 bool mfma_supported(int dk, int dv) {
-  return (dk == 64 && dv == 128) || (dk == 128 && dv == 128) ||
-         (dk == 128 && dv == 256) || (dk == 256 && dv == 256) || (dk == 256 && dv == 512);
+  return (dk == 64 && dv == 128) || (dk == 128 && dv == 128) || (dk == 128 && dv == 256) ||
+         (dk == 256 && dv == 256) || (dk == 256 && dv == 512);
 }
 
-// dv columns per workgroup in the chunkwise kernels: the fp32 state slice
+// dv columns per workgroup in the segment-state pass: the fp32 state slice
 // DK x DVW lives in the accumulators of 8 waves (<= 64 registers each).
-static int chunk_dvw(int dk, int dv) {
+static int state_dvw(int dk, int dv) {
   int dvw = dv;
   while ((long long)dk * dvw > 128 * 256) dvw /= 2;
   return dvw;
@@ -603,76 +900,93 @@ static int chunk_dvw(int dk, int dv) {
 
 ChunkPlan chunk_plan(int B, int H, int L, int dk, int dv, int chunk) {
   ChunkPlan p;
-  const int nsplit = dv / chunk_dvw(dk, dv);
+  const int nsplit = dv / state_dvw(dk, dv);
   const int nchunks = (L + chunk - 1) / chunk;
   const int units = B * H * nsplit;
-  const int target = 256;  // one workgroup per CU
+  const int target = 256;  // segment-state pass: about one workgroup per CU
   int nseg = (target + units - 1) / units;
   if (nseg > nchunks) nseg = nchunks;
   if (nseg < 1) nseg = 1;
   p.seg_chunks = (nchunks + nseg - 1) / nseg;
   p.nseg = (nchunks + p.seg_chunks - 1) / p.seg_chunks;
-  p.ws_bytes = (size_t)B * H * p.nseg * dk * dv * sizeof(float);
+  const size_t SZ = (size_t)dk * dv;
+  p.seg_bytes = (size_t)B * H * p.nseg * SZ * sizeof(float);
+  // states that fit one workgroup's accumulators stay in registers through a
+  // segment; larger ones are stored per chunk (bf16) for the query-block kernel
+  const bool in_regs = nsplit == 1;
+  p.sinT_bytes = in_regs ? 0 : (size_t)B * H * p.nseg * SZ * 2;
+  p.loc_bytes = in_regs ? 0 : (size_t)B * H * nchunks * SZ * 2;
+  p.ws_bytes = p.seg_bytes + p.sinT_bytes + p.loc_bytes;
   return p;
 }
 
 template <int DK, int DV>
-static hipError_t run_parallel(const RetArgs &a, hipStream_t st) {
-  TaskGeom geo{1, 1, 1, (a.L + BT - 1) / BT, 0};
-  geo.ntasks = a.B * a.H * geo.nqb;
-  if (a.use_gn)
-    hipLaunchKernelGGL((tile_kernel<DK, DV, true, true>), dim3(xcd_grid(geo.ntasks)), dim3(NT), 0, st, a, geo,
-                       nullptr);
+static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const uint16_t *sinT, const uint16_t *locT,
+                              hipStream_t st) {
+  geo.nqb = par ? (a.L + BT - 1) / BT : (a.chunk + BT - 1) / BT;
+  geo.nchunks = par ? 1 : (a.L + a.chunk - 1) / a.chunk;
+  geo.ntasks = a.B * a.H * geo.nchunks * geo.nqb;
+  const dim3 grid(xcd_grid(geo.ntasks));
+  if (par && a.use_gn)
+    hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid, dim3(NT), 0, st, a, geo, sinT, locT);
+  else if (par)
+    hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, sinT, locT);
+  else if (a.use_gn)
+    hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid, dim3(NT), 0, st, a, geo, sinT, locT);
   else
-    hipLaunchKernelGGL((tile_kernel<DK, DV, true, false>), dim3(xcd_grid(geo.ntasks)), dim3(NT), 0, st, a, geo,
-                       nullptr);
+    hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, sinT, locT);
   return hipGetLastError();
 }
 
-template <int DK, int DVW>
-static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, float *ws, const float *state_in,
+template <int DK, int DV>
+static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, const float *state_in,
                                 float *state_out, hipStream_t st) {
-  TaskGeom geo{p.nseg, p.seg_chunks, a.dv / DVW, 1, 0};
+  constexpr int DVW1 = (DK * DV > 128 * 256) ? (128 * 256) / DK : DV;
+  constexpr bool IN_REGS = DVW1 == DV;
+  float *seg = (float *)ws;
+  uint16_t *sinT = IN_REGS ? nullptr : (uint16_t *)(ws + p.seg_bytes);
+  uint16_t *locT = IN_REGS ? nullptr : (uint16_t *)(ws + p.seg_bytes + p.sinT_bytes);
+  TaskGeom geo{p.nseg, p.seg_chunks, DV / DVW1, 1, 0, (a.L + a.chunk - 1) / a.chunk};
   geo.ntasks = a.B * a.H * geo.nseg * geo.nsplit;
-  const unsigned nblk = xcd_grid(geo.ntasks);
-  hipLaunchKernelGGL((seg_state_kernel<DK, DVW>), dim3(nblk), dim3(NT), 0, st, a, geo, ws);
+  hipLaunchKernelGGL((seg_state_kernel<DK, DVW1>), dim3(xcd_grid(geo.ntasks)), dim3(NT), 0, st, a, geo, seg, locT);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long n4 = (long long)a.dk * a.dv / 4;
-  const int gx = (int)((n4 + 255) / 256);
-  hipLaunchKernelGGL(seg_scan_kernel, dim3(gx, a.B * a.H), dim3(256), 0, st, a, geo, ws, state_in, state_out);
+  hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)((n4 + 255) / 256), a.B * a.H), dim3(256), 0, st, a, geo, seg,
+                     sinT, state_in, state_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  RetArgs a2 = a;
-  const bool split_gn = a.use_gn && DVW != a.dv;
-  if (split_gn) a2.use_gn = 0;
-  if (a.use_gn)
-    hipLaunchKernelGGL((tile_kernel<DK, DVW, false, true>), dim3(nblk), dim3(NT), 0, st, a2, geo, ws);
-  else
-    hipLaunchKernelGGL((tile_kernel<DK, DVW, false, false>), dim3(nblk), dim3(NT), 0, st, a2, geo, ws);
-  e = hipGetLastError();
-  if (e != hipSuccess || !split_gn) return e;
-  hipLaunchKernelGGL(gn_rows_kernel, dim3((unsigned)((long long)a.B * a.H * a.L)), dim3(256), 0, st, a);
-  return hipGetLastError();
+  if constexpr (IN_REGS) {
+    geo.ntasks = a.B * a.H * geo.nseg;
+    const dim3 grid(xcd_grid(geo.ntasks));
+    if (a.use_gn)
+      hipLaunchKernelGGL((seg_out_kernel<DK, DV, true>), grid, dim3(NT), 0, st, a, geo, seg);
+    else
+      hipLaunchKernelGGL((seg_out_kernel<DK, DV, false>), grid, dim3(NT), 0, st, a, geo, seg);
+    return hipGetLastError();
+  } else {
+    return run_qblocks<DK, DV>(a, geo, false, sinT, locT, st);
+  }
 }
 
 hipError_t launch_mfma_parallel(const RetArgs &a, hipStream_t st) {
-  if (a.dk == 64 && a.dv == 128) return run_parallel<64, 128>(a, st);
-  if (a.dk == 128 && a.dv == 128) return run_parallel<128, 128>(a, st);
-  if (a.dk == 128 && a.dv == 256) return run_parallel<128, 256>(a, st);
-  if (a.dk == 256 && a.dv == 256) return run_parallel<256, 256>(a, st);
-  if (a.dk == 256 && a.dv == 512) return run_parallel<256, 512>(a, st);
+  TaskGeom geo{1, 1, 1, 1, 0, 1};
+  if (a.dk == 64 && a.dv == 128) return run_qblocks<64, 128>(a, geo, true, nullptr, nullptr, st);
+  if (a.dk == 128 && a.dv == 128) return run_qblocks<128, 128>(a, geo, true, nullptr, nullptr, st);
+  if (a.dk == 128 && a.dv == 256) return run_qblocks<128, 256>(a, geo, true, nullptr, nullptr, st);
+  if (a.dk == 256 && a.dv == 256) return run_qblocks<256, 256>(a, geo, true, nullptr, nullptr, st);
+  if (a.dk == 256 && a.dv == 512) return run_qblocks<256, 512>(a, geo, true, nullptr, nullptr, st);
   return hipErrorNotSupported;
 }
 
 hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &p, void *ws, const float *state_in,
                                  float *state_out, hipStream_t st) {
-  float *w = (float *)ws;
+  char *w = (char *)ws;
   if (a.dk == 64 && a.dv == 128) return run_chunkwise<64, 128>(a, p, w, state_in, state_out, st);
   if (a.dk == 128 && a.dv == 128) return run_chunkwise<128, 128>(a, p, w, state_in, state_out, st);
   if (a.dk == 128 && a.dv == 256) return run_chunkwise<128, 256>(a, p, w, state_in, state_out, st);
-  if (a.dk == 256 && a.dv == 256) return run_chunkwise<256, 128>(a, p, w, state_in, state_out, st);
-  if (a.dk == 256 && a.dv == 512) return run_chunkwise<256, 128>(a, p, w, state_in, state_out, st);
+  if (a.dk == 256 && a.dv == 256) return run_chunkwise<256, 256>(a, p, w, state_in, state_out, st);
+  if (a.dk == 256 && a.dv == 512) return run_chunkwise<256, 512>(a, p, w, state_in, state_out, st);
   return hipErrorNotSupported;
 }
 

@@ -6,9 +6,9 @@
 // Launch sequence on the caller's stream:
 //   1. one GEMM for [W_Q | W_K | W_V | W_G]: Q, K, V scattered head-major
 //      [B,H,L,d] (bf16), swish(X W_G) token-major [B*L, H*dv] (bf16);
-//   2. chunkwise retention (MFMA kernels), fp32 output token-major [B,L,H,dv];
-//   3. per (token, head) GroupNorm times the gate -> Z bf16 [B*L, H*dv];
-//   4. GEMM Z . W_O -> y [B*L, d_model] bf16.
+//   2. chunkwise retention (MFMA kernels) with the per-(token, head) GroupNorm
+//      and the gate applied in the epilogue -> Z bf16 token-major [B*L, H*dv];
+//   3. GEMM Z . W_O -> y [B*L, d_model] bf16.
 #include <string.h>
 
 #include <cmath>
@@ -24,7 +24,7 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct MsrLayout {
-  size_t q, k, v, gate, o32, z, cw, total;
+  size_t q, k, v, gate, z, cw, total;
 };
 
 MsrLayout msr_layout(int B, int L, int H, int dk, int dv, int chunk) {
@@ -39,8 +39,6 @@ MsrLayout msr_layout(int B, int L, int H, int dk, int dv, int chunk) {
   off += align256(T * H * dv * 2);
   m.gate = off;
   off += align256(T * H * dv * 2);
-  m.o32 = off;
-  off += align256(T * H * dv * 4);
   m.z = off;
   off += align256(T * H * dv * 2);
   m.cw = off;
@@ -49,57 +47,7 @@ MsrLayout msr_layout(int B, int L, int H, int dk, int dv, int chunk) {
   return m;
 }
 
-// One wave per (token, head) row: GroupNorm over dv, times the gate.
-__global__ __launch_bounds__(256) void gn_gate_kernel(const float *o32, const uint16_t *gate, uint16_t *z,
-                                                      long long rows, int dv, float eps) {
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const float *x = o32 + row * dv;
-  constexpr int MAXV = RETENTION_MAX_DV / 256;
-  float4 v[MAXV];
-  float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < MAXV; ++c) {
-    const int j = 4 * lane + 256 * c;
-    v[c] = j < dv ? *(const float4 *)(x + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-    s += v[c].x + v[c].y + v[c].z + v[c].w;
-  }
-  const float mean = wave_sum(s) / (float)dv;
-  float q = 0.0f;
-#pragma unroll
-  for (int c = 0; c < MAXV; ++c) {
-    const int j = 4 * lane + 256 * c;
-    if (j < dv) {
-      const float a = v[c].x - mean, b = v[c].y - mean, cc = v[c].z - mean, d = v[c].w - mean;
-      q += a * a + b * b + cc * cc + d * d;
-    }
-  }
-  const float inv = 1.0f / sqrtf(wave_sum(q) / (float)dv + eps);
-#pragma unroll
-  for (int c = 0; c < MAXV; ++c) {
-    const int j = 4 * lane + 256 * c;
-    if (j < dv) {
-      const uint2 gg = *(const uint2 *)(gate + row * dv + j);
-      const float g0 = bf2f(gg.x & 0xffff), g1 = bf2f(gg.x >> 16), g2 = bf2f(gg.y & 0xffff), g3 = bf2f(gg.y >> 16);
-      uint2 o;
-      o.x = pack_bf2(g0 * (v[c].x - mean) * inv, g1 * (v[c].y - mean) * inv);
-      o.y = pack_bf2(g2 * (v[c].z - mean) * inv, g3 * (v[c].w - mean) * inv);
-      *(uint2 *)(z + row * dv + j) = o;
-    }
-  }
-}
-
 }  // namespace
-
-namespace ret {
-hipError_t launch_gn_gate(const RetArgs &a, const float *o32, uint16_t *z, hipStream_t st) {
-  const long long rows = (long long)a.B * a.L * a.H;
-  hipLaunchKernelGGL(gn_gate_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, o32, a.gate, z, rows, a.dv,
-                     a.gn_eps);
-  return hipGetLastError();
-}
-}  // namespace ret
 
 // Defined in abi.hip: records the message returned by retention_last_error().
 ret_status_t retention_fail_(ret_status_t s, const char *msg);
@@ -152,7 +100,6 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
   char *ws = (char *)workspace;
   uint16_t *qh = (uint16_t *)(ws + m.q), *kh = (uint16_t *)(ws + m.k), *vh = (uint16_t *)(ws + m.v);
   uint16_t *gs = (uint16_t *)(ws + m.gate), *z = (uint16_t *)(ws + m.z);
-  float *o32 = (float *)(ws + m.o32);
 
   // 1. projections
   GemmArgs g1;
@@ -168,13 +115,14 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
   hipError_t e = launch_gemm_bf16(g1, st);
   if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
 
-  // 2. chunkwise retention, fp32 out, token-major
+  // 2.+3. chunkwise retention with GroupNorm and the gate in the epilogue -> Z
   RetArgs a;
   memset(&a, 0, sizeof(a));
   a.q = qh;
   a.k = kh;
   a.v = vh;
-  a.o = o32;
+  a.o = z;
+  a.gate = gs;
   a.q_sn = dk;
   a.q_sh = (long long)L * dk;
   a.q_sb = (long long)H * L * dk;
@@ -184,6 +132,9 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
   a.o_sn = (long long)H * dv;
   a.o_sh = dv;
   a.o_sb = (long long)L * H * dv;
+  a.g_sn = a.o_sn;
+  a.g_sh = a.o_sh;
+  a.g_sb = a.o_sb;
   a.pos0 = pos0;
   a.B = B;
   a.H = H;
@@ -192,20 +143,15 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
   a.dv = dv;
   a.chunk = chunk;
   a.in_bf16 = 1;
-  a.out_bf16 = 0;
+  a.out_bf16 = 1;
   a.use_theta = theta != nullptr;
-  a.use_gn = 0;
+  a.use_gn = 1;
   a.gn_eps = gn_eps;
   for (int h = 0; h < H; ++h) a.gamma[h] = gamma[h];
   if (theta)
     for (int i = 0; i < dk / 2; ++i) a.theta[i] = theta[i];
   const ChunkPlan plan = chunk_plan(B, H, L, dk, dv, chunk);
   e = launch_mfma_chunkwise(a, plan, ws + m.cw, nullptr, nullptr, st);
-  if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
-
-  // 3. GroupNorm per (token, head), times swish(X W_G)
-  a.gate = gs;
-  e = launch_gn_gate(a, o32, z, st);
   if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
 
   // 4. output projection
