@@ -140,7 +140,12 @@ struct TileIO {
     c8 = (rest / NG) * CG + lo;
   }
 
+  // Buffer loads through a resource whose range ends after row valid-1: rows at
+  // or past `valid` read as zero (hardware range check), with no branches and
+  // 32-bit offsets.  Rows are `stride` elements apart.
   __device__ __forceinline__ void fetch(const uint16_t *src, long long stride, int valid) {
+    const int nbytes = valid > 0 ? (int)((long long)valid * stride * 2) : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nbytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int idx = threadIdx.x + NT * i;
@@ -148,9 +153,13 @@ struct TileIO {
       item(idx, tg, c8);
 #pragma unroll
       for (int r = 0; r < TPT; ++r) {
-        const int t = TPT * tg + r;
-        raw[i][r] = (idx < ITEMS && t < valid) ? *(const uint4 *)(src + (long long)t * stride + 8 * c8)
-                                                : make_uint4(0u, 0u, 0u, 0u);
+        const int off = ((TPT * tg + r) * (int)stride + 8 * c8) * 2;
+        if (ITEMS % NT == 0 || idx < ITEMS) {
+          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+          raw[i][r] = make_uint4(x.x, x.y, x.z, x.w);
+        } else {
+          raw[i][r] = make_uint4(0u, 0u, 0u, 0u);
+        }
       }
     }
   }
@@ -677,23 +686,21 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
                                                   0);
         vio.commit_trans(Vt);
         __syncthreads();
-        // prefetch the next visit: next key block of this query block, else the
-        // next query block (of this chunk, or the first of the next chunk)
-        if (kb < qb) {
-          const int n0 = k0 + BT;
-          kio.fetch(k + (long long)n0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - n0));
-          vio.fetch(v + (long long)n0 * a.v_sn, a.v_sn, min(BT, c0 + Cc - n0));
-        } else {
-          int nc0 = c0, nq0 = q0 + BT;
-          if (qb + 1 >= nqb_c) {
-            nc0 = c0 + Cc;
-            nq0 = nc0;
-          }
-          if (nc0 < t_hi) {
-            const int nCc = min(a.chunk, a.L - nc0);
-            qio.fetch(q + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nc0 + nCc - nq0));
-            kio.fetch(k + (long long)nc0 * a.q_sn, a.q_sn, min(BT, nCc));
-            vio.fetch(v + (long long)nc0 * a.v_sn, a.v_sn, min(BT, nCc));
+        // next visit: next key block of this query block, else the first key block
+        // of the next query block (of this chunk, or of the next chunk).  Its loads
+        // are issued in two parts -- K before the scores, V before PV -- so the
+        // memory system absorbs them while the MFMAs run.
+        int nk0 = k0 + BT, nend = c0 + Cc;
+        if (kb == qb) {
+          nk0 = last_qb ? c0 + Cc : c0;
+          nend = min(a.L, nk0 + a.chunk);
+        }
+        const bool has_next = nk0 < t_hi;
+        if (has_next) {
+          kio.fetch(k + (long long)nk0 * a.q_sn, a.q_sn, min(BT, nend - nk0));
+          if (kb == qb) {  // and the next query block's tile
+            const int nq0 = last_qb ? nk0 : q0 + BT;
+            qio.fetch(q + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nend - nq0));
           }
         }
 #pragma unroll
@@ -714,6 +721,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           for (int i = 0; i < 4; ++i) p[i] = sc[i] * (gdel * dt[dp - i]);
           *(u32x2 *)(Ps + (16 * qblk + l16) * LDT + 32 * kh + 16 * kb16 + 4 * g) = pack4(p[0], p[1], p[2], p[3]);
         }
+        if (has_next) vio.fetch(v + (long long)nk0 * a.v_sn, a.v_sn, min(BT, nend - nk0));
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
