@@ -71,6 +71,24 @@ def _src_sha():
     return h.hexdigest()[:16]
 
 
+def _alg_bytes_chunkwise():
+    """Q, K, V read once, O (bf16) and the final fp32 state written once."""
+    from workloads import CHUNKWISE_32K as wl
+    return 2 * (2 * wl.B * wl.H * wl.L * wl.dk) + 2 * wl.B * wl.H * wl.L * wl.dv * 2 + 4 * wl.B * wl.H * wl.dk * wl.dv
+
+
+def _alg_bytes_decode():
+    """fp32 state read and written, bf16 q, k, v read and o written, per step."""
+    from workloads import DECODE as wl
+    return 2 * 4 * wl.B * wl.H * wl.dk * wl.dv + 2 * 2 * wl.B * wl.H * wl.dk + 2 * 2 * wl.B * wl.H * wl.dv
+
+
+def _alg_bytes_parallel():
+    """Q, K, V read once, O (bf16) written once."""
+    from workloads import PARALLEL_2K as wl
+    return 2 * 2 * wl.B * wl.H * wl.L * wl.dk + 2 * 2 * wl.B * wl.H * wl.L * wl.dv
+
+
 def bench_chunkwise(steps, warmup):
     import torch
     import retentive_network_scale_amd as rn
@@ -87,9 +105,7 @@ def bench_chunkwise(steps, warmup):
     t = _time_calls(call, steps, warmup)
     per_call = t / steps
     tokens = wl.B * wl.L
-    # algorithmic: Q, K, V read once, O (bf16) and the final fp32 state written once
-    bytes_alg = 2 * (2 * wl.B * wl.H * wl.L * wl.dk) + 2 * wl.B * wl.H * wl.L * wl.dv * 2 + \
-        4 * wl.B * wl.H * wl.dk * wl.dv
+    bytes_alg = _alg_bytes_chunkwise()
     C = wl.chunk
     flops_alg = wl.B * wl.H * (wl.L / C) * 2 * (C * (C + 1) / 2 * (wl.dk + wl.dv) + 2 * C * wl.dk * wl.dv)
     achieved = bytes_alg / per_call / 1e9
@@ -98,7 +114,7 @@ def bench_chunkwise(steps, warmup):
         "tokens_per_s": tokens / per_call, "ms_per_step": per_call * 1e3, "tokens": tokens,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "retention_chunkwise (seg_state + seg_scan + tile_kernel launches)",
+                     "kernel": "retention_chunkwise call: seg_state_kernel + seg_scan_kernel + seg_out_kernel (durations summed)",
                      "algorithmic_bytes_per_call": bytes_alg},
         "mfma": {"algorithmic_tflop_per_call": flops_alg / 1e12,
                  "achieved_tflops": flops_alg / per_call / 1e12,
@@ -132,7 +148,7 @@ def bench_decode(warmup_loops=1):
     torch.cuda.synchronize()
     t = _time_calls(loop, 1, 0)
     per_step = t / wl.steps
-    bytes_step = 2 * 4 * wl.B * wl.H * wl.dk * wl.dv + 2 * 2 * wl.B * wl.H * wl.dk + 2 * 2 * wl.B * wl.H * wl.dv
+    bytes_step = _alg_bytes_decode()
     achieved = bytes_step / per_step / 1e9
     return {"tokens_per_s": wl.B * wl.steps / t, "ms_per_step": per_step * 1e3, "steps": wl.steps,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -155,7 +171,7 @@ def bench_parallel(steps, warmup):
     return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / BF16_PEAK_TFLOPS, "traffic": _read_traffic("parallel_2k"),
-                         "kernel": "tile_kernel<256,512,parallel,split>",
+                         "kernel": "qblock_kernel<256,512,parallel,split>",
                          "algorithmic_tflop_per_call": flops / 1e12}}
 
 
@@ -183,6 +199,99 @@ def bench_msr(steps, warmup):
                          "algorithmic_tflop_per_call": (gemm + ret) / 1e12}}
 
 
+COPY_BYTES = 1 << 29  # 512 MiB: the plain streaming kernel that calibrates FETCH_SIZE / WRITE_SIZE
+
+
+def copy_calibration(reps=3):
+    """A plain elementwise copy (torch.neg, bf16) of COPY_BYTES read + COPY_BYTES
+    written, larger than the last-level cache, so that a rocprofv3 PMC run of this
+    command can convert the TCC FETCH_SIZE / WRITE_SIZE counters to HBM bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+# Which dispatches make one call of each workload, for the PMC summary:
+# (kernels summed per call, kernel that occurs once per call).
+_PMC_GROUPS = {
+    "chunkwise_32k": ("ret::", ("seg_out_kernel", "qblock_kernel")),
+    "decode_step": ("vec_step_kernel", ("vec_step_kernel",)),
+    "parallel_2k": ("qblock_kernel", ("qblock_kernel",)),
+}
+
+
+def pmc_summary(name, fetch_csv, write_csv, command):
+    """Turns two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then
+    WRITE_SIZE, in KiB per dispatch) of a `bench.py --only ... --copy-calibration`
+    run into profiles/traffic_<name>.txt: HBM bytes per call, scaled by the
+    counters' reading for the calibration copy."""
+    import csv
+    import collections
+    incl, once = _PMC_GROUPS[name]
+
+    def read(path, counter):
+        per_kernel = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                per_kernel[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        copy = [v for k, lst in per_kernel.items() if "neg_kernel" in k for v in lst]
+        calls = sum(len(lst) for k, lst in per_kernel.items() if any(o in k for o in once))
+        total = sum(sum(lst) for k, lst in per_kernel.items() if incl in k)
+        names = sorted(k for k in per_kernel if incl in k)
+        if not copy or not calls:
+            raise SystemExit(f"{path}: no calibration copy or no {once} dispatches")
+        copy_kib = sum(copy) / len(copy)
+        return total / calls, copy_kib, calls, names
+    f_kib, f_copy, calls, names = read(fetch_csv, "FETCH_SIZE")
+    w_kib, w_copy, _, _ = read(write_csv, "WRITE_SIZE")
+    f_fac, w_fac = COPY_BYTES / (f_copy * 1024), COPY_BYTES / (w_copy * 1024)
+    hbm = f_kib * 1024 * f_fac + w_kib * 1024 * w_fac
+    alg = {"chunkwise_32k": _alg_bytes_chunkwise(), "decode_step": _alg_bytes_decode(),
+           "parallel_2k": _alg_bytes_parallel()}[name]
+    out = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    with open(out, "w") as fh:
+        fh.write(f"# HBM traffic per call of {name}: rocprofv3 PMC FETCH_SIZE and WRITE_SIZE (KiB per dispatch),\n"
+                 f"# summed over the dispatches of one call ({calls} calls), each scaled by the factor that maps\n"
+                 f"# the counter's reading for a plain bf16 copy of {COPY_BYTES} bytes (torch.neg) to those bytes.\n")
+        for c in command:
+            fh.write(f"# command: {c}\n")
+        fh.write("# kernels: " + "; ".join(n[:90] for n in names) + "\n")
+        fh.write(f"fetch_kib_per_call = {f_kib:.1f}\nwrite_kib_per_call = {w_kib:.1f}\n"
+                 f"copy_fetch_kib = {f_copy:.1f}\ncopy_write_kib = {w_copy:.1f}\n"
+                 f"fetch_factor = {f_fac:.4f}\nwrite_factor = {w_fac:.4f}\n"
+                 f"hbm_bytes_per_call = {hbm:.0f}\nalgorithmic_bytes_per_call = {alg}\n"
+                 f"traffic_over_algorithmic = {hbm / alg:.3f}\nsrc_sha = {_src_sha()}\n")
+    print(open(out).read())
+
+
+def stats_summary(trace_dir, command):
+    """Markdown tables of a rocprofv3 --kernel-trace --stats run: the kernel_stats.csv
+    as written, then the kernel_trace.csv grouped by kernel and grid size (one
+    group per workload shape)."""
+    import csv
+    import glob
+    import collections
+    stats = glob.glob(os.path.join(trace_dir, "*_kernel_stats.csv"))[0]
+    trace = glob.glob(os.path.join(trace_dir, "*_kernel_trace.csv"))[0]
+    print(f"command: `{command}`\n")
+    print("| kernel | calls | avg us | min us | max us | % of GPU time |\n|---|---|---|---|---|---|")
+    for r in csv.DictReader(open(stats)):
+        print(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    groups = collections.OrderedDict()
+    for r in csv.DictReader(open(trace)):
+        key = (r["Kernel_Name"][:80], int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]), r["VGPR_Count"],
+               r["Accum_VGPR_Count"], r["Scratch_Size"], r["LDS_Block_Size"])
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("\n| kernel | workgroups | arch VGPR | acc VGPR | scratch B | LDS B | calls | avg us | min us |\n"
+          "|---|---|---|---|---|---|---|---|---|")
+    for (name, wg, vg, ag, sc, lds), d in groups.items():
+        print(f"| `{name}` | {wg} | {vg} | {ag} | {sc} | {lds} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} |")
+
+
 def cpu_baseline(sample_tokens):
     """The fp64 oracle (chunkwise form, chunk 256) on the first `sample_tokens`
     tokens of all 8 heads of the long-context workload, timed on host cores."""
@@ -193,12 +302,17 @@ def cpu_baseline(sample_tokens):
     qs, ks, vs = (oracle.as_f64(t[:, :, :n]) for t in (q, k, v))
     g, th = wl.gamma(), wl.theta()
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    t0 = time.perf_counter()
-    oracle.chunkwise(qs, ks, vs, g, wl.chunk, th)
-    dt = time.perf_counter() - t0
-    return {"value": wl.B * n / dt, "unit": "tokens/s", "cores": min(threads, wl.B * wl.H), "kind": "oracle",
+    reps, t0 = 0, time.perf_counter()
+    while True:  # whole passes until about 10 s of CPU work
+        oracle.chunkwise(qs, ks, vs, g, wl.chunk, th)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or reps >= 50:
+            break
+    return {"value": reps * wl.B * n / dt, "unit": "tokens/s", "cores": min(threads, wl.B * wl.H), "kind": "oracle",
             "sample": f"fp64 chunkwise oracle (chunk {wl.chunk}) on tokens 0..{n - 1} of all {wl.H} heads of "
-                      f"the L=32768 workload, {dt:.1f} s; OpenMP over the {wl.B * wl.H} (b, h) units"}
+                      f"the L=32768 workload, {reps} passes in {dt:.1f} s; OpenMP over the {wl.B * wl.H} "
+                      f"(b, h) units"}
 
 
 def main():
@@ -209,7 +323,22 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline chunkwise workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "msr"],
+                    help="run one workload and print its figures (for profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run the plain copy that calibrates the PMC byte counters")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("NAME", "FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_NAME.txt from two rocprofv3 PMC runs (no GPU needed)")
+    ap.add_argument("--pmc-command", action="append", default=[], help="command line recorded in the summary")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
+                    help="print a rocprofv3 --kernel-trace --stats output folder as tables (no GPU needed)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, args.pmc_command)
+        return
+    if args.stats_summary:
+        stats_summary(*args.stats_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -220,6 +349,15 @@ def main():
         sys.exit(2)
     import retentive_network_scale_amd as rn
     rn.lib()  # fails loudly if the HIP library is not built
+    if args.copy_calibration:
+        _log(f"calibration copy of {COPY_BYTES} bytes")
+        copy_calibration()
+    if args.only and args.only != "chunkwise":
+        _log(args.only)
+        res = {"decode": lambda: bench_decode(), "parallel": lambda: bench_parallel(args.steps, args.warmup),
+               "msr": lambda: bench_msr(args.steps, args.warmup)}[args.only]()
+        print(json.dumps({"workload": args.only, **res}), flush=True)
+        return
     from workloads import CHUNKWISE_32K
     _log("chunkwise L=32768")
     ch = bench_chunkwise(args.steps, args.warmup)
@@ -232,14 +370,14 @@ def main():
                    "chunk": CHUNKWISE_32K.chunk},
         "roofline": ch["roofline"], "chunkwise_mfma": ch["mfma"],
     }
-    if not args.no_extra:
+    if not (args.no_extra or args.only):
         _log("decode B128 H16, 1024 steps")
         line["decode"] = bench_decode()
         _log("parallel B8 H8 L2048")
         line["parallel"] = bench_parallel(max(3, args.steps // 2), args.warmup)
         _log("msr layer B4 L4096")
         line["msr_layer"] = bench_msr(max(3, args.steps // 4), args.warmup)
-    if not args.no_cpu:
+    if not (args.no_cpu or args.only):
         _log(f"cpu baseline ({args.cpu_tokens} tokens)")
         line["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
     print(json.dumps(line), flush=True)
