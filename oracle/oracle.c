@@ -16,7 +16,7 @@
  *   [P1] "RetNet dual-mode hands-on manual", lanjinlin.com.cn/news/2041318.
  *        Sec. 1 (the decay matrix), Sec. 3.1 (parallel/recurrent equivalence).
  *
- * Conventions (readings of the pages; each is documented in the design doc):
+ * Conventions (readings of the pages where they leave a choice open):
  *   - Arrays are row-major fp64.  Q, K: [B,H,L,dk]; V, O: [B,H,L,dv];
  *     state S: [B,H,dk,dv].  Token n of a call sits at absolute position
  *     p = pos0 + n (0-based).

@@ -4,9 +4,9 @@ sum, sampled entries of the final state), plus closed-form and property checks
 that hold at any size.
 
 Workloads (seeded synthetic inputs from `workloads`):
-  2. parallel   B8 H8 L2048 dk256 dv512 bf16, GroupNorm
-  3. chunkwise  B1 H8 L32768 dk128 dv256 chunk256 bf16
-  4. decode     B128 H16 dk128 dv256: 512-token chunkwise prefill + 1024 steps
+  parallel   B8 H8 L2048 dk256 dv512 bf16, GroupNorm
+  chunkwise  B1 H8 L32768 dk128 dv256 chunk256 bf16
+  decode     B128 H16 dk128 dv256: 512-token chunkwise prefill + 1024 steps
 """
 import numpy as np
 import pytest
@@ -86,7 +86,7 @@ def test_chunkwise_32k_closed_form():
 
 
 def test_decode_workload_end_to_end_sampled():
-    """Workload 4: GPU chunkwise prefill (positions 0..511, chunk 256) into the fp32
+    """Decode workload: GPU chunkwise prefill (positions 0..511, chunk 256) into the fp32
     state, then 1024 GPU decode steps (positions 512..1535).  Every step's output of
     sampled (sequence, head) pairs, and their final states, against the oracle's
     recurrent form over all 1536 tokens."""

@@ -52,7 +52,7 @@ def test_msr_zero_gate():
 
 
 def test_msr_full_size_sampled():
-    """Workload 5 (X [4,4096,2048], 8 heads, dk 256, dv 512, chunk 512) at full size;
+    """The MSR layer workload (X [4,4096,2048], 8 heads, dk 256, dv 512, chunk 512) at full size;
     sampled output rows checked against the oracle, which computes each from the
     defining sums (only the tokens up to the latest sampled one are needed: the
     layer is causal)."""

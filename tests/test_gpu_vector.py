@@ -23,7 +23,7 @@ def _gpu(*ts):
 
 
 def test_tiny_fp32_three_forms():
-    """Workload 1: B1 H2 L64 dk=dv=16 fp32, chunk 16: every form within 1e-4 of the oracle."""
+    """Tiny workload: B1 H2 L64 dk=dv=16 fp32, chunk 16: every form within 1e-4 of the oracle."""
     q, k, v = TINY.qkv()
     g, th = TINY.gamma(), TINY.theta()
     ref = oracle.parallel(q, k, v, g, th)

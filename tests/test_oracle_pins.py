@@ -101,7 +101,7 @@ def test_mask_structure_and_rotation_phase():
 
 # ---------------------------------------------------------------- P1, P2, P5: three forms agree
 def test_tiny_workload_three_forms_agree():
-    """Workload 1 (B1 H2 L64 dk=dv=16, chunk 16): parallel = recurrent = chunkwise."""
+    """Tiny workload (B1 H2 L64 dk=dv=16, chunk 16): parallel = recurrent = chunkwise."""
     q, k, v = TINY.qkv()
     g, th = TINY.gamma(), TINY.theta()
     op = oracle.parallel(q, k, v, g, th)

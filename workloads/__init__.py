@@ -6,7 +6,8 @@ constants and rotation frequencies).  Both the GPU tests and the oracle-side
 checks take their inputs from here; nothing here depends on either side.
 
 Recipe: ``torch.Generator('cpu').manual_seed(1000 * c + j)`` where ``c`` is the
-workload number (1..5, ``c = 0`` for ad-hoc test shapes with an explicit seed)
+workload's seed group (tiny 1, parallel 2, chunkwise 3, decode 4, MSR layer 5;
+ad-hoc test shapes pass an explicit seed)
 and ``j`` the tensor's index in a fixed draw order (Q=0, K=1, V=2, W_Q=3, W_K=4,
 W_V=5, W_G=6, W_O=7); ``torch.randn`` in fp32, scaled in fp32, then cast to the
 workload dtype (round to nearest even for bf16).  Values are i.i.d. Gaussian:
@@ -52,7 +53,7 @@ class RetentionWorkload:
     dtype: torch.dtype
     scale: float
     gn_eps: Optional[float]
-    config_id: int
+    seed_group: int
     pos0: int = 0
 
     def gamma(self):
@@ -62,7 +63,7 @@ class RetentionWorkload:
         return rotation_theta(self.dk)
 
     def qkv(self, seed_base: Optional[int] = None):
-        base = 1000 * self.config_id if seed_base is None else seed_base
+        base = 1000 * self.seed_group if seed_base is None else seed_base
         q = randn((self.B, self.H, self.L, self.dk), base + 0, self.scale, self.dtype)
         k = randn((self.B, self.H, self.L, self.dk), base + 1, self.scale, self.dtype)
         v = randn((self.B, self.H, self.L, self.dv), base + 2, self.scale, self.dtype)
@@ -73,13 +74,13 @@ class RetentionWorkload:
         return self.B * self.L
 
 
-# workload 1: tiny check, all three forms (fp32)
+# tiny check, all three forms (fp32)
 TINY = RetentionWorkload("tiny-fp32 B1 H2 L64 dk16 dv16 chunk16", 1, 2, 64, 16, 16, 16,
                          torch.float32, 1.0, None, 1)
-# workload 2: parallel form, bf16, GroupNorm on the output
+# parallel form, bf16, GroupNorm on the output
 PARALLEL_2K = RetentionWorkload("parallel B8 H8 L2048 dk256 dv512 bf16 +GN", 8, 8, 2048, 256, 512,
                                 2048, torch.bfloat16, 256 ** -0.5, 1e-5, 2)
-# workload 3: chunkwise, long context
+# chunkwise form, long context
 CHUNKWISE_32K = RetentionWorkload("chunkwise B1 H8 L32768 dk128 dv256 chunk256 bf16", 1, 8, 32768,
                                   128, 256, 256, torch.bfloat16, 128 ** -0.5, None, 3)
 
@@ -95,7 +96,7 @@ class DecodeWorkload:
     steps: int = 1024
     chunk: int = 256
     scale: float = 128 ** -0.5
-    config_id: int = 4
+    seed_group: int = 4
 
     def gamma(self):
         return multiscale_gamma(self.H)
@@ -104,7 +105,7 @@ class DecodeWorkload:
         return rotation_theta(self.dk)
 
     def prefill_qkv(self):
-        b = 1000 * self.config_id
+        b = 1000 * self.seed_group
         q = randn((self.B, self.H, self.prefill, self.dk), b + 0, self.scale, torch.bfloat16)
         k = randn((self.B, self.H, self.prefill, self.dk), b + 1, self.scale, torch.bfloat16)
         v = randn((self.B, self.H, self.prefill, self.dv), b + 2, self.scale, torch.bfloat16)
@@ -113,7 +114,7 @@ class DecodeWorkload:
     def step_qkv(self, steps: Optional[int] = None):
         """All decode-step inputs at once: [steps, B, H, d]."""
         n = self.steps if steps is None else steps
-        b = 1000 * self.config_id
+        b = 1000 * self.seed_group
         q = randn((n, self.B, self.H, self.dk), b + 3, self.scale, torch.bfloat16)
         k = randn((n, self.B, self.H, self.dk), b + 4, self.scale, torch.bfloat16)
         v = randn((n, self.B, self.H, self.dv), b + 5, self.scale, torch.bfloat16)
@@ -135,7 +136,7 @@ class MSRWorkload:
     chunk: int = 512
     gn_eps: float = 1e-5
     w_std: float = 0.02
-    config_id: int = 5
+    seed_group: int = 5
 
     def gamma(self):
         return multiscale_gamma(self.H)
@@ -146,7 +147,7 @@ class MSRWorkload:
     def inputs(self, seed_base: Optional[int] = None):
         """x [B,L,d_model]; weights stored [out, in]: w_q, w_k [H*dk, d_model],
         w_v, w_g [H*dv, d_model], w_o [d_model, H*dv]."""
-        b = 1000 * self.config_id if seed_base is None else seed_base
+        b = 1000 * self.seed_group if seed_base is None else seed_base
         bf = torch.bfloat16
         x = randn((self.B, self.L, self.d_model), b + 0, 1.0, bf)
         w_q = randn((self.H * self.dk, self.d_model), b + 3, self.w_std, bf)
