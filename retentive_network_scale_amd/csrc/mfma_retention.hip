@@ -164,6 +164,44 @@ struct TileIO {
     }
   }
 
+  // The loads of fetch() for token slot r only (fetch == fetch_row for r = 0..TPT-1),
+  // so that a tile's loads can be spread between other instructions.
+  __device__ __forceinline__ void fetch_row(const uint16_t *src, long long stride, int valid, int r) {
+    const int nbytes = valid > 0 ? (int)((long long)valid * stride * 2) : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nbytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      int tg, c8;
+      item(idx, tg, c8);
+      const int off = ((TPT * tg + r) * (int)stride + 8 * c8) * 2;
+      if (ITEMS % NT == 0 || idx < ITEMS) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        raw[i][r] = make_uint4(x.x, x.y, x.z, x.w);
+      } else {
+        raw[i][r] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+
+  // Reload a tile already in LDS, token-major rows of pitch ldr (8-byte aligned).
+  __device__ __forceinline__ void load_lds(const uint16_t *src, int ldr) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      int tg, c8;
+      item(idx, tg, c8);
+#pragma unroll
+      for (int r = 0; r < TPT; ++r) {
+        if (ITEMS % NT == 0 || idx < ITEMS) {
+          const uint16_t *sr = src + (TPT * tg + r) * ldr + 8 * c8;
+          const u32x2 lo = *(const u32x2 *)sr, hi = *(const u32x2 *)(sr + 4);
+          raw[i][r] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+      }
+    }
+  }
+
   // rows:  dst[t * ldr + col]            (token-major, bf16; lo part to dstLo when LO)
   // trans: dstT[col * LDT + t] * zeta_t  (token-minor), zeta_t = gamma^(zoff - t) when `zeta`
   // Rotation (rot): token t of the tile sits at absolute position p0 + t.
@@ -310,9 +348,20 @@ static inline unsigned xcd_grid(int ntasks) { return (unsigned)(((ntasks + 7) / 
 // Epilogue of a 64-query block held as O^T accumulators: optional GroupNorm over
 // all DV values of each (token, head) row (every wave holds RW of them), optional
 // bf16 gate multiply, store (bf16 or fp32) with the output strides of `a`.
-template <int RB, int RW, int DV>
+// Column order of a wave's O^T rows.  With PAIR (two 16-row blocks per wave), row
+// m of block rb holds dv offset 8*(m/4) + 4*rb + m%4 of the wave's 32 columns, so
+// the D-layout accumulators of a lane -- rows 4g..4g+3 of both blocks -- are 8
+// consecutive columns: one 16-byte store per query row.  The same order is
+// applied wherever a dv index enters an MFMA operand (V^T rows, state columns).
+template <bool PAIR>
+__device__ __forceinline__ int dv_of(int rb, int m) {
+  return PAIR ? 8 * (m >> 2) + 4 * rb + (m & 3) : 16 * rb + m;
+}
+
+template <int RB, int RW, int DV, bool PAIR = false>
 __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB][4], float (*red)[BT], int b, int h,
                                                int q0, int nvalid, long long obase, int w, int g, int l16) {
+  static_assert(!PAIR || RB == 2, "paired column order needs two row blocks");
   if (a.use_gn) {
     float mean[4], inv[4];
 #pragma unroll
@@ -353,6 +402,37 @@ __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB]
     for (int qb4 = 0; qb4 < 4; ++qb4)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = (ot[rb][qb4] - mean[qb4]) * inv[qb4];
+  }
+  if constexpr (PAIR) {
+#pragma unroll
+    for (int qb4 = 0; qb4 < 4; ++qb4) {
+      const int r = 16 * qb4 + l16;
+      if (r < nvalid) {
+        const long long ro = obase + (long long)(q0 + r) * a.o_sn;
+        const int col = w * RW + 8 * g;
+        float x[8] = {ot[0][qb4][0], ot[0][qb4][1], ot[0][qb4][2], ot[0][qb4][3],
+                      ot[1][qb4][0], ot[1][qb4][1], ot[1][qb4][2], ot[1][qb4][3]};
+        if (a.gate) {
+          const long long go = (long long)b * a.g_sb + (long long)h * a.g_sh + (long long)(q0 + r) * a.g_sn + col;
+          const u32x4 gg = *(const u32x4 *)(a.gate + go);
+          const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] *= __uint_as_float(gw[e] << 16);
+            x[2 * e + 1] *= __uint_as_float(gw[e] & 0xffff0000u);
+          }
+        }
+        if (a.out_bf16) {
+          *(u32x4 *)((uint16_t *)a.o + ro + col) =
+              u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
+        } else {
+          float *dst = (float *)a.o + ro + col;
+          *(float4 *)dst = make_float4(x[0], x[1], x[2], x[3]);
+          *(float4 *)(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+        }
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int qb4 = 0; qb4 < 4; ++qb4) {
@@ -560,15 +640,22 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
 // last query block runs (it visits them all), so the cross terms of the
 // earlier blocks see S_c.  Global loads of the next visit are in flight
 // during the current one.
-template <int DK, int DV, bool SPLIT>
+// RES (chunks of at most KRES key blocks, no hi/lo split): the chunk's rotated
+// keys stay in LDS, so each key block is fetched and rotated once, at its
+// diagonal visit; the update's zeta-scaled transposed copy of an earlier block
+// is rebuilt from LDS.
+constexpr int KRES = 4;  // resident key blocks: chunks up to 256 tokens
+template <int DK, int DV, bool SPLIT, bool RES>
 __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, const float *seg_state) {
   using T = Tile<DK, DV>;
   constexpr int LDQ = T::LDQ, RW = T::RW, RB = T::RB, KS = T::KS, DKB = T::DKB;
+  constexpr bool PAIR = RB == 2;
+  static_assert(!(RES && SPLIT), "resident keys carry no lo part");
   // Qs (rotated query block, bf16) is read only before the key loop and Kt
   // (zeta-scaled transposed keys of the update) only inside it: shared storage.
   constexpr int QK_SZ = BT * LDQ > DK * LDT ? BT * LDQ : DK * LDT;
   __shared__ __attribute__((aligned(16))) uint16_t QKs[QK_SZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BT * LDQ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[(RES ? KRES : 1) * BT * LDQ];
   __shared__ __attribute__((aligned(16))) uint16_t KsL[SPLIT ? BT * LDQ : 8];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * LDT];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[BT * LDT];
@@ -610,7 +697,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          st[dkb][rb][i] = S_in[(long long)(16 * dkb + 4 * g + i) * DV + w * RW + 16 * rb + l16];
+          st[dkb][rb][i] = S_in[(long long)(16 * dkb + 4 * g + i) * DV + w * RW + dv_of<PAIR>(rb, l16)];
   }
   TileIO<DK> qio, kio;
   TileIO<DV> vio;
@@ -677,13 +764,21 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
         const bool upd = carry && last_qb;
         const int delta = qb - kb;
         const float gdel = delta ? dpow(lg, 64 * (delta - 1)) : 1.0f;
+        uint16_t *const Kb = RES ? Ks + kb * BT * LDQ : Ks;
         __syncthreads();
-        if (upd)
-          kio.template commit<true, true, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Ks, LDQ, KsL, Kt, true, lg,
-                                                 Cc - 1 - (k0 - c0));
-        else
-          kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Ks, LDQ, KsL, nullptr, false, 0.f,
-                                                  0);
+        if (!RES || kb == qb) {
+          if (upd)
+            kio.template commit<true, true, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Kb, LDQ, KsL, Kt, true, lg,
+                                                   Cc - 1 - (k0 - c0));
+          else
+            kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Kb, LDQ, KsL, nullptr, false,
+                                                    0.f, 0);
+        } else if (upd) {  // resident block: zeta-scaled transposed copy from LDS
+          TileIO<DK> kres;
+          kres.load_lds(Kb, LDQ);
+          kres.template commit<false, true, false>(false, 0, theta_s, rev_s, nullptr, LDQ, nullptr, Kt, true, lg,
+                                                   Cc - 1 - (k0 - c0));
+        }
         vio.commit_trans(Vt);
         __syncthreads();
         // next visit: next key block of this query block, else the first key block
@@ -696,7 +791,17 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           nend = min(a.L, nk0 + a.chunk);
         }
         const bool has_next = nk0 < t_hi;
-        if (has_next) {
+        if constexpr (RES) {
+          // keys are needed from memory only at diagonal visits: the next one is
+          // the next query block's, and both tiles start at the same token
+          if (kb == qb) {
+            const int nq0 = last_qb ? nk0 : q0 + BT;
+            if (nq0 < t_hi) {
+              kio.fetch(k + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nend - nq0));
+              qio.fetch(q + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nend - nq0));
+            }
+          }
+        } else if (has_next) {
           kio.fetch(k + (long long)nk0 * a.q_sn, a.q_sn, min(BT, nend - nk0));
           if (kb == qb) {  // and the next query block's tile
             const int nq0 = last_qb ? nk0 : q0 + BT;
@@ -708,7 +813,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 ak = ld_op(Ks + (32 * kh + 16 * kb16 + l16) * LDQ, 32 * ks, g);
+            const u32x4 ak = ld_op(Kb + (32 * kh + 16 * kb16 + l16) * LDQ, 32 * ks, g);
             sc = mfma(ak, qreg[ks], sc);
             if constexpr (SPLIT) {
               sc = mfma(ld_op(KsL + (32 * kh + 16 * kb16 + l16) * LDQ, 32 * ks, g), qreg[ks], sc);
@@ -727,7 +832,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
         for (int ks = 0; ks < 2; ++ks) {
           u32x4 av[RB];
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) av[rb] = ld_op(Vt + (w * RW + 16 * rb + l16) * LDT, 32 * ks, g);
+          for (int rb = 0; rb < RB; ++rb) av[rb] = ld_op(Vt + (w * RW + dv_of<PAIR>(rb, l16)) * LDT, 32 * ks, g);
 #pragma unroll
           for (int qb4 = 0; qb4 < 4; ++qb4) {
             const u32x4 bp = ld_op(Ps + (16 * qb4 + l16) * LDT, 32 * ks, g);
@@ -745,7 +850,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           }
         }
       }
-      epilogue_store<RB, RW, DV>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
+      epilogue_store<RB, RW, DV, PAIR>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
     }
   }
 }
@@ -871,22 +976,31 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, 
     float4 *base = (float4 *)(ws + (long long)bh * geo.nseg * SZ);
     uint16_t *tb = sinT ? sinT + (long long)bh * geo.nseg * SZ : nullptr;
     const int row = (int)(4 * e / a.dv), col = (int)(4 * e % a.dv);  // element (dk row, dv col..col+3)
-    for (int s = 0; s < geo.nseg; ++s) {
-      const float4 d = base[(long long)s * n4 + e];
-      base[(long long)s * n4 + e] = run;
-      if (sinT) {
-        uint16_t *t = tb + (long long)s * SZ + row;
-        t[(long long)(col + 0) * a.dk] = f2bf(run.x);
-        t[(long long)(col + 1) * a.dk] = f2bf(run.y);
-        t[(long long)(col + 2) * a.dk] = f2bf(run.z);
-        t[(long long)(col + 3) * a.dk] = f2bf(run.w);
+    constexpr int SB = 8;  // segments whose loads are in flight together
+    for (int s0 = 0; s0 < geo.nseg; s0 += SB) {
+      float4 d[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        if (s0 + j < geo.nseg) d[j] = base[(long long)(s0 + j) * n4 + e];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const int s = s0 + j;
+        if (s >= geo.nseg) break;
+        base[(long long)s * n4 + e] = run;
+        if (sinT) {
+          uint16_t *t = tb + (long long)s * SZ + row;
+          t[(long long)(col + 0) * a.dk] = f2bf(run.x);
+          t[(long long)(col + 1) * a.dk] = f2bf(run.y);
+          t[(long long)(col + 2) * a.dk] = f2bf(run.z);
+          t[(long long)(col + 3) * a.dk] = f2bf(run.w);
+        }
+        const int len = min(a.L, (s + 1) * seg_len) - s * seg_len;
+        const float gm = len == seg_len ? g_full : dpow(lg, len);
+        run.x = gm * run.x + d[j].x;
+        run.y = gm * run.y + d[j].y;
+        run.z = gm * run.z + d[j].z;
+        run.w = gm * run.w + d[j].w;
       }
-      const int len = min(a.L, (s + 1) * seg_len) - s * seg_len;
-      const float gm = len == seg_len ? g_full : dpow(lg, len);
-      run.x = gm * run.x + d.x;
-      run.y = gm * run.y + d.y;
-      run.z = gm * run.z + d.z;
-      run.w = gm * run.w + d.w;
     }
     if (state_out) ((float4 *)(state_out + (long long)bh * SZ))[e] = run;
   }
@@ -968,9 +1082,11 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
     geo.ntasks = a.B * a.H * geo.nseg;
     const dim3 grid(xcd_grid(geo.ntasks));
     if (a.use_gn)
-      hipLaunchKernelGGL((seg_out_kernel<DK, DV, true>), grid, dim3(NT), 0, st, a, geo, seg);
+      hipLaunchKernelGGL((seg_out_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, seg);
+    else if (a.chunk <= KRES * BT)
+      hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, true>), grid, dim3(NT), 0, st, a, geo, seg);
     else
-      hipLaunchKernelGGL((seg_out_kernel<DK, DV, false>), grid, dim3(NT), 0, st, a, geo, seg);
+      hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, seg);
     return hipGetLastError();
   } else {
     return run_qblocks<DK, DV>(a, geo, false, sinT, locT, st);
