@@ -423,8 +423,10 @@ __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB]
           }
         }
         if (a.out_bf16) {
-          *(u32x4 *)((uint16_t *)a.o + ro + col) =
-              u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
+          // streaming store: the output is not read again by this call
+          __builtin_nontemporal_store(
+              u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])},
+              (u32x4 *)((uint16_t *)a.o + ro + col));
         } else {
           float *dst = (float *)a.o + ro + col;
           *(float4 *)dst = make_float4(x[0], x[1], x[2], x[3]);
@@ -858,10 +860,26 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
 // ---------------------------------------------------------------- pass 1: segment states
 // Walks the segment chunk by chunk from a zero state:
 //   S <- gamma^Cc S + sum_i gamma^(Cc-1-i) k_i^T v_i     (per chunk)
-// 64 tokens at a time, double-buffered in LDS with the next block's global
-// loads in flight.  Before every chunk after the first it stores S (the local
-// state entering that chunk) as bf16 S^T[dv][dk] in locT; at the end it stores
-// the segment's own state (fp32, [dk][dv]) in seg_state.
+// 64 tokens at a time, double-buffered in LDS, with the global loads of the
+// next two blocks in flight (two register sets, used alternately).  Before
+// every chunk after the first it stores S (the local state entering that
+// chunk) as bf16 S^T[dv][dk] in locT; at the end it stores the segment's own
+// state (fp32, [dk][dv]) in seg_state.
+
+// Position of a 64-token block: its first token, and its chunk's start and length.
+struct BlockPos {
+  int k0, c0, Cc;
+  __device__ __forceinline__ void advance(int L, int chunk) {
+    k0 += BT;
+    if (k0 >= c0 + Cc) {
+      c0 += Cc;
+      k0 = c0;
+      Cc = min(chunk, L - c0);
+    }
+  }
+  __device__ __forceinline__ int valid() const { return min(BT, c0 + Cc - k0); }
+};
+
 template <int DK, int DVW>
 __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, float *seg_state, uint16_t *locT) {
   using T = Tile<DK, DVW>;
@@ -893,47 +911,55 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
   for (int dkb = 0; dkb < DKB; ++dkb)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  TileIO<DK> kio;
-  TileIO<DVW> vio;
-  kio.fetch(k + (long long)t_lo * a.q_sn, a.q_sn, min(BT, min(a.chunk, t_hi - t_lo)));
-  vio.fetch(v + (long long)t_lo * a.v_sn, a.v_sn, min(BT, min(a.chunk, t_hi - t_lo)));
+  TileIO<DK> kio[2];
+  TileIO<DVW> vio[2];
+  // pf: the next block to fetch; a block past the segment fetches no rows
+  BlockPos cur{t_lo, t_lo, min(a.chunk, a.L - t_lo)}, pf = cur;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int nv = pf.k0 < t_hi ? pf.valid() : 0;
+    kio[s].fetch(k + (long long)pf.k0 * a.q_sn, a.q_sn, nv);
+    vio[s].fetch(v + (long long)pf.k0 * a.v_sn, a.v_sn, nv);
+    pf.advance(a.L, a.chunk);
+  }
   int buf = 0;
-  for (int c = c_lo; c < c_hi; ++c) {
-    const int c0 = c * a.chunk, Cc = min(a.chunk, a.L - c0);
-    if (c > c_lo) {
-      // local state entering chunk c -> locT (bf16, S^T[dv][dk]) when requested; then
-      // decay it over the chunk
-      if (locT) {
-        uint16_t *dst = locT + ((long long)bh * geo.nchunks + c) * DK * a.dv;
+  // two blocks per iteration, one per register set
+  for (bool more = true; more;) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (cur.k0 >= t_hi) {
+        more = false;
+        break;
+      }
+      if (cur.k0 == cur.c0 && cur.c0 > t_lo) {
+        // local state entering this chunk -> locT (bf16, S^T[dv][dk]) when
+        // requested; then decay it over the chunk
+        if (locT) {
+          uint16_t *dst = locT + ((long long)bh * geo.nchunks + cur.c0 / a.chunk) * DK * a.dv;
+#pragma unroll
+          for (int dkb = 0; dkb < DKB; ++dkb)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              *(u32x2 *)(dst + (long long)(split * DVW + w * RW + 16 * rb + l16) * DK + 16 * dkb + 4 * g) =
+                  pack4(st[dkb][rb][0], st[dkb][rb][1], st[dkb][rb][2], st[dkb][rb][3]);
+        }
+        const float gc = dpow(lg, cur.Cc);
 #pragma unroll
         for (int dkb = 0; dkb < DKB; ++dkb)
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            *(u32x2 *)(dst + (long long)(split * DVW + w * RW + 16 * rb + l16) * DK + 16 * dkb + 4 * g) =
-                pack4(st[dkb][rb][0], st[dkb][rb][1], st[dkb][rb][2], st[dkb][rb][3]);
+          for (int rb = 0; rb < RB; ++rb) st[dkb][rb] *= gc;
       }
-      const float gc = dpow(lg, Cc);
-#pragma unroll
-      for (int dkb = 0; dkb < DKB; ++dkb)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) st[dkb][rb] *= gc;
-    }
-    for (int k0 = c0; k0 < c0 + Cc; k0 += BT, buf ^= 1) {
       // buffer `buf` was last read two blocks ago; the barrier of the previous
       // block ordered those reads before this write
-      kio.template commit<false, true, false>(a.use_theta, a.pos0 + k0, theta_s, rev_s, nullptr, 0, nullptr, Kt[buf],
-                                              true, lg, c0 + Cc - 1 - k0);
-      vio.commit_trans(Vt[buf]);
+      kio[s].template commit<false, true, false>(a.use_theta, a.pos0 + cur.k0, theta_s, rev_s, nullptr, 0, nullptr,
+                                                 Kt[buf], true, lg, cur.c0 + cur.Cc - 1 - cur.k0);
+      vio[s].commit_trans(Vt[buf]);
       __syncthreads();
-      // prefetch the next block: this chunk's next, else the next chunk's first
-      int n0 = k0 + BT, nend = c0 + Cc;
-      if (n0 >= nend) {
-        n0 = c0 + Cc;
-        nend = min(a.L, n0 + a.chunk);
-      }
-      if (n0 < t_hi) {
-        kio.fetch(k + (long long)n0 * a.q_sn, a.q_sn, min(BT, nend - n0));
-        vio.fetch(v + (long long)n0 * a.v_sn, a.v_sn, min(BT, nend - n0));
+      {  // this register set now takes the block two ahead
+        const int nv = pf.k0 < t_hi ? pf.valid() : 0;
+        kio[s].fetch(k + (long long)pf.k0 * a.q_sn, a.q_sn, nv);
+        vio[s].fetch(v + (long long)pf.k0 * a.v_sn, a.v_sn, nv);
+        pf.advance(a.L, a.chunk);
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -947,6 +973,8 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
           for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = mfma(ak, bv[rb], st[dkb][rb]);
         }
       }
+      buf ^= 1;
+      cur.advance(a.L, a.chunk);
     }
   }
   float *dst = seg_state + ((long long)bh * geo.nseg + seg) * DK * a.dv + split * DVW;
