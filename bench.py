@@ -122,6 +122,30 @@ def bench_chunkwise(steps, warmup):
     }
 
 
+SWEEP_CHUNKS = (64, 128, 256, 512, 1024, 2048)
+
+
+def bench_chunk_sweep(steps, warmup):
+    """Chunkwise tokens/s on the L=32768 workload for each chunk size (same inputs,
+    same outputs up to rounding; the chunk only moves work between the direct
+    intra-chunk sums and the state)."""
+    import torch
+    import retentive_network_scale_amd as rn
+    from workloads import CHUNKWISE_32K as wl
+    q, k, v = (t.cuda() for t in wl.qkv())
+    g, th = wl.gamma(), wl.theta()
+    out = torch.empty((wl.B, wl.H, wl.L, wl.dv), dtype=torch.bfloat16, device="cuda")
+    state = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    res = {}
+    for chunk in SWEEP_CHUNKS:
+        ws = torch.empty(rn.retention_chunkwise_workspace_bytes(wl.B, wl.H, wl.L, wl.dk, wl.dv, chunk),
+                         dtype=torch.uint8, device="cuda")
+        t = _time_calls(lambda: rn.retention_chunkwise(q, k, v, g, chunk, th, state_out=state, out=out,
+                                                       workspace=ws), steps, warmup)
+        res[str(chunk)] = {"tokens_per_s": wl.B * wl.L * steps / t, "ms_per_step": t / steps * 1e3}
+    return res
+
+
 def bench_decode(warmup_loops=1):
     import torch
     import retentive_network_scale_amd as rn
@@ -323,7 +347,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline chunkwise workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "msr"],
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "msr", "sweep"],
                     help="run one workload and print its figures (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the plain copy that calibrates the PMC byte counters")
@@ -355,7 +379,8 @@ def main():
     if args.only and args.only != "chunkwise":
         _log(args.only)
         res = {"decode": lambda: bench_decode(), "parallel": lambda: bench_parallel(args.steps, args.warmup),
-               "msr": lambda: bench_msr(args.steps, args.warmup)}[args.only]()
+               "msr": lambda: bench_msr(args.steps, args.warmup),
+               "sweep": lambda: {"chunk_sweep": bench_chunk_sweep(args.steps, args.warmup)}}[args.only]()
         print(json.dumps({"workload": args.only, **res}), flush=True)
         return
     from workloads import CHUNKWISE_32K
@@ -377,6 +402,8 @@ def main():
         line["parallel"] = bench_parallel(max(3, args.steps // 2), args.warmup)
         _log("msr layer B4 L4096")
         line["msr_layer"] = bench_msr(max(3, args.steps // 4), args.warmup)
+        _log("chunk-size sweep")
+        line["chunk_sweep"] = bench_chunk_sweep(max(5, args.steps // 2), args.warmup)
     if not (args.no_cpu or args.only):
         _log(f"cpu baseline ({args.cpu_tokens} tokens)")
         line["cpu_baseline"] = cpu_baseline(args.cpu_tokens)

@@ -61,6 +61,30 @@ def test_chunkwise_32k_sampled_rows_and_state():
     assert torch.isfinite(o.float()).all()
 
 
+@pytest.mark.parametrize("chunk", [64, 128, 512, 1024, 2048])
+def test_chunkwise_32k_chunk_sizes_sampled(chunk):
+    """The chunk-size sweep's configurations (same inputs, other chunk sizes,
+    including ones that take the non-resident-key path): sampled rows and final
+    state entries against the oracle's defining sums."""
+    wl = CHUNKWISE_32K
+    q, k, v = wl.qkv()
+    g, th = wl.gamma(), wl.theta()
+    o, s = rn.retention_chunkwise(q.to(DEV), k.to(DEV), v.to(DEV), g, chunk, th, state_out=True)
+    torch.cuda.synchronize()
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    rng = np.random.default_rng(100 + chunk)
+    idx = [(0, 0, 0), (0, 7, wl.L - 1), (0, 2, chunk - 1), (0, 2, chunk), (0, 5, 3 * chunk + 17)]
+    idx += [(0, int(rng.integers(wl.H)), int(rng.integers(wl.L))) for _ in range(7)]
+    ref = oracle.rows(qn, kn, vn, g, idx, th)
+    got = np.stack([o[b, h, n].float().cpu().numpy() for b, h, n in idx])
+    _tol.assert_bf16(got, ref, slice_dims=1, what=f"chunk {chunk} sampled rows")
+    sidx = [(0, h, int(rng.integers(wl.dk)), int(rng.integers(wl.dv))) for h in range(wl.H) for _ in range(2)]
+    sref = oracle.state_entries(kn, vn, g, sidx, th)
+    sgot = np.array([s[b, h, a, c].item() for b, h, a, c in sidx])
+    rel = np.linalg.norm(sgot - sref) / np.linalg.norm(sref)
+    assert rel <= _tol.BF16_REL_L2, f"chunk {chunk}: final state entries rel-L2 {rel:.3e}"
+
+
 def test_chunkwise_32k_closed_form():
     """q_n = k_m = u, v = 1 at L = 32768 with rotation: the defining sum is a geometric
     series, o_n[j] = sum_i |z_i|^2 Re[(1 - w_i^(n+1)) / (1 - w_i)], w_i = gamma e^{i theta_i}.
