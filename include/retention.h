@@ -140,8 +140,14 @@ ret_status_t retention_recurrent_step(const void *q, const void *k, const void *
  *   x   : [B,L,d_model] bf16         y   : [B,L,d_model] bf16
  *   w_q, w_k : [H*dk, d_model] bf16   w_v, w_g : [H*dv, d_model] bf16
  *   w_o : [d_model, H*dv] bf16
- * UNSUPPORTED unless d_model % 64 == 0 and (dk, dv) is one of the MFMA pairs
- * listed under retention_parallel.
+ * UNSUPPORTED unless d_model, H*dk and H*dv are multiples of 128 and (dk, dv) is
+ * one of the MFMA pairs listed under retention_parallel.
+ * The four projections and W_O are plain GEMMs run through hipBLASLt (this
+ * library's own GEMM kernel where hipBLASLt offers no algorithm); the first
+ * call on a device creates that device's hipBLASLt handle, kept until the
+ * process ends.  The workspace (size from msr_layer_fwd_workspace_bytes) holds
+ * the projections [B*L][2 H dk + 2 H dv], the gated normalised heads
+ * [B*L][H*dv], the chunkwise workspace and 32 MiB for hipBLASLt.
  */
 size_t msr_layer_fwd_workspace_bytes(int B, int L, int d_model, int H, int dk, int dv,
                                      int chunk);

@@ -50,7 +50,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(workers) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-L/opt/rocm/lib", "-lhipblaslt",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

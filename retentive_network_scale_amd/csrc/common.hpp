@@ -18,6 +18,7 @@ struct RetArgs {
   const void *q, *k, *v;
   void *o;
   const uint16_t *gate;  // optional bf16 multiplier applied after GroupNorm (gated layer)
+  int gate_swish;        // the multiplier is swish(gate) = gate / (1 + exp(-gate)) instead of gate
   long long q_sb, q_sh, q_sn;
   long long v_sb, v_sh, v_sn;
   long long o_sb, o_sh, o_sn;

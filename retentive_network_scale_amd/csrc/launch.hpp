@@ -51,4 +51,10 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_bf16(const GemmArgs &args, hipStream_t st);
 
+// Plain bf16 GEMM through hipBLASLt (blaslt.hip): C[t][n] = sum_k X[t][k] W[n][k]
+// for t < T, n < N, row-major with row stride ldc.  hipErrorNotSupported when
+// hipBLASLt has no algorithm for the shape within ws_bytes of workspace.
+hipError_t blaslt_gemm_nt(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, int N, int K, int ldc,
+                          void *ws, size_t ws_bytes, hipStream_t st);
+
 }  // namespace ret

@@ -348,6 +348,12 @@ static inline unsigned xcd_grid(int ntasks) { return (unsigned)(((ntasks + 7) / 
 // Epilogue of a 64-query block held as O^T accumulators: optional GroupNorm over
 // all DV values of each (token, head) row (every wave holds RW of them), optional
 // bf16 gate multiply, store (bf16 or fp32) with the output strides of `a`.
+// Gate multiplier from a gate value: swish(x) = x / (1 + e^-x) when `swish`
+// (the gated layer's swish(X W_G)), else x itself.
+__device__ __forceinline__ float gate_value(float x, int swish) {
+  return swish ? x / (1.0f + __expf(-x)) : x;
+}
+
 // Column order of a wave's O^T rows.  With PAIR (two 16-row blocks per wave), row
 // m of block rb holds dv offset 8*(m/4) + 4*rb + m%4 of the wave's 32 columns, so
 // the D-layout accumulators of a lane -- rows 4g..4g+3 of both blocks -- are 8
@@ -418,8 +424,8 @@ __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB]
           const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x[2 * e] *= __uint_as_float(gw[e] << 16);
-            x[2 * e + 1] *= __uint_as_float(gw[e] & 0xffff0000u);
+            x[2 * e] *= gate_value(__uint_as_float(gw[e] << 16), a.gate_swish);
+            x[2 * e + 1] *= gate_value(__uint_as_float(gw[e] & 0xffff0000u), a.gate_swish);
           }
         }
         if (a.out_bf16) {
@@ -448,10 +454,10 @@ __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB]
         if (a.gate) {
           const long long go = (long long)b * a.g_sb + (long long)h * a.g_sh + (long long)(q0 + r) * a.g_sn + col;
           const u32x2 gg = *(const u32x2 *)(a.gate + go);
-          x[0] *= __uint_as_float(gg.x << 16);
-          x[1] *= __uint_as_float(gg.x & 0xffff0000u);
-          x[2] *= __uint_as_float(gg.y << 16);
-          x[3] *= __uint_as_float(gg.y & 0xffff0000u);
+          x[0] *= gate_value(__uint_as_float(gg.x << 16), a.gate_swish);
+          x[1] *= gate_value(__uint_as_float(gg.x & 0xffff0000u), a.gate_swish);
+          x[2] *= gate_value(__uint_as_float(gg.y << 16), a.gate_swish);
+          x[3] *= gate_value(__uint_as_float(gg.y & 0xffff0000u), a.gate_swish);
         }
         if (a.out_bf16)
           *(u32x2 *)((uint16_t *)a.o + ro + col) = pack4(x[0], x[1], x[2], x[3]);

@@ -4,11 +4,13 @@
 //   head_i = Retention(X, gamma_i);  Y = GroupNorm_h(Concat(heads));
 //   MSR(X) = (swish(X W_G) (.) Y) W_O
 // Launch sequence on the caller's stream:
-//   1. one GEMM for [W_Q | W_K | W_V | W_G]: Q, K, V scattered head-major
-//      [B,H,L,d] (bf16), swish(X W_G) token-major [B*L, H*dv] (bf16);
-//   2. chunkwise retention (MFMA kernels) with the per-(token, head) GroupNorm
-//      and the gate applied in the epilogue -> Z bf16 token-major [B*L, H*dv];
-//   3. GEMM Z . W_O -> y [B*L, d_model] bf16.
+//   1. four plain GEMMs X W_Q, X W_K, X W_V, X W_G into one token-major bf16
+//      buffer P[B*L][2 H dk + 2 H dv] (hipBLASLt; this library's GEMM kernel when
+//      hipBLASLt has no algorithm for a shape);
+//   2. chunkwise retention (MFMA kernels) reading Q, K, V and the gate straight
+//      from P through strides, with the per-(token, head) GroupNorm and the swish
+//      gate applied in the epilogue -> Z bf16 token-major [B*L, H*dv];
+//   3. GEMM Z . W_O -> y [B*L, d_model] bf16 (as in 1).
 #include <string.h>
 
 #include <cmath>
@@ -23,28 +25,41 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr size_t BLAS_WS = 32u << 20;  // hipBLASLt workspace
+
 struct MsrLayout {
-  size_t q, k, v, gate, z, cw, total;
+  size_t proj, z, cw, blas, total;
 };
 
 MsrLayout msr_layout(int B, int L, int H, int dk, int dv, int chunk) {
   MsrLayout m;
   const size_t T = (size_t)B * L;
   size_t off = 0;
-  m.q = off;
-  off += align256(T * H * dk * 2);
-  m.k = off;
-  off += align256(T * H * dk * 2);
-  m.v = off;
-  off += align256(T * H * dv * 2);
-  m.gate = off;
-  off += align256(T * H * dv * 2);
+  m.proj = off;
+  off += align256(T * (2 * (size_t)H * dk + 2 * (size_t)H * dv) * 2);
   m.z = off;
   off += align256(T * H * dv * 2);
   m.cw = off;
   off += align256(chunk_plan(B, H, L, dk, dv, chunk).ws_bytes);
+  m.blas = off;
+  off += BLAS_WS;
   m.total = off;
   return m;
+}
+
+// C[t][n] = sum_k X[t][k] W[n][k] (row stride ldc): hipBLASLt, else this library's GEMM kernel.
+hipError_t plain_gemm(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, int N, int K, int ldc, void *blas_ws,
+                      hipStream_t st) {
+  hipError_t e = blaslt_gemm_nt(X, W, C, T, N, K, ldc, blas_ws, BLAS_WS, st);
+  if (e != hipErrorNotSupported) return e;
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A = X;
+  g.M = T;
+  g.K = K;
+  g.nseg = 1;
+  g.seg[0] = GemmSeg{W, N, GEMM_PLAIN, C, (long long)ldc, 0, 0, 0};
+  return launch_gemm_bf16(g, st);
 }
 
 }  // namespace
@@ -98,43 +113,44 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
   }
   hipStream_t st = (hipStream_t)hip_stream;
   char *ws = (char *)workspace;
-  uint16_t *qh = (uint16_t *)(ws + m.q), *kh = (uint16_t *)(ws + m.k), *vh = (uint16_t *)(ws + m.v);
-  uint16_t *gs = (uint16_t *)(ws + m.gate), *z = (uint16_t *)(ws + m.z);
+  uint16_t *proj = (uint16_t *)(ws + m.proj), *z = (uint16_t *)(ws + m.z);
+  const long long NP = 2LL * H * dk + 2LL * H * dv;  // row length of P
+  const long long cq = 0, ck = (long long)H * dk, cv = 2LL * H * dk, cg = cv + (long long)H * dv;
 
-  // 1. projections
-  GemmArgs g1;
-  memset(&g1, 0, sizeof(g1));
-  g1.A = (const uint16_t *)x;
-  g1.M = (int)T;
-  g1.K = d_model;
-  g1.nseg = 4;
-  g1.seg[0] = GemmSeg{(const uint16_t *)w_q, H * dk, GEMM_HEADS, qh, 0, L, H, dk};
-  g1.seg[1] = GemmSeg{(const uint16_t *)w_k, H * dk, GEMM_HEADS, kh, 0, L, H, dk};
-  g1.seg[2] = GemmSeg{(const uint16_t *)w_v, H * dv, GEMM_HEADS, vh, 0, L, H, dv};
-  g1.seg[3] = GemmSeg{(const uint16_t *)w_g, H * dv, GEMM_SWISH, gs, (long long)H * dv, L, H, dv};
-  hipError_t e = launch_gemm_bf16(g1, st);
-  if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  // 1. projections into P
+  const uint16_t *X = (const uint16_t *)x;
+  const struct {
+    const void *w;
+    long long col;
+    int n;
+  } proj_w[4] = {{w_q, cq, H * dk}, {w_k, ck, H * dk}, {w_v, cv, H * dv}, {w_g, cg, H * dv}};
+  for (const auto &pw : proj_w) {
+    hipError_t e = plain_gemm(X, (const uint16_t *)pw.w, proj + pw.col, (int)T, pw.n, d_model, (int)NP, ws + m.blas,
+                              st);
+    if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  }
 
-  // 2.+3. chunkwise retention with GroupNorm and the gate in the epilogue -> Z
+  // 2. chunkwise retention with GroupNorm and the swish gate in the epilogue -> Z
   RetArgs a;
   memset(&a, 0, sizeof(a));
-  a.q = qh;
-  a.k = kh;
-  a.v = vh;
+  a.q = proj + cq;
+  a.k = proj + ck;
+  a.v = proj + cv;
   a.o = z;
-  a.gate = gs;
-  a.q_sn = dk;
-  a.q_sh = (long long)L * dk;
-  a.q_sb = (long long)H * L * dk;
-  a.v_sn = dv;
-  a.v_sh = (long long)L * dv;
-  a.v_sb = (long long)H * L * dv;
+  a.gate = proj + cg;
+  a.gate_swish = 1;
+  a.q_sn = NP;
+  a.q_sh = dk;
+  a.q_sb = (long long)L * NP;
+  a.v_sn = NP;
+  a.v_sh = dv;
+  a.v_sb = (long long)L * NP;
+  a.g_sn = NP;
+  a.g_sh = dv;
+  a.g_sb = (long long)L * NP;
   a.o_sn = (long long)H * dv;
   a.o_sh = dv;
   a.o_sb = (long long)L * H * dv;
-  a.g_sn = a.o_sn;
-  a.g_sh = a.o_sh;
-  a.g_sb = a.o_sb;
   a.pos0 = pos0;
   a.B = B;
   a.H = H;
@@ -151,18 +167,11 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
   if (theta)
     for (int i = 0; i < dk / 2; ++i) a.theta[i] = theta[i];
   const ChunkPlan plan = chunk_plan(B, H, L, dk, dv, chunk);
-  e = launch_mfma_chunkwise(a, plan, ws + m.cw, nullptr, nullptr, st);
+  hipError_t e = launch_mfma_chunkwise(a, plan, ws + m.cw, nullptr, nullptr, st);
   if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
 
-  // 4. output projection
-  GemmArgs g2;
-  memset(&g2, 0, sizeof(g2));
-  g2.A = z;
-  g2.M = (int)T;
-  g2.K = H * dv;
-  g2.nseg = 1;
-  g2.seg[0] = GemmSeg{(const uint16_t *)w_o, d_model, GEMM_PLAIN, y, (long long)d_model, L, H, dv};
-  e = launch_gemm_bf16(g2, st);
+  // 3. output projection
+  e = plain_gemm(z, (const uint16_t *)w_o, (uint16_t *)y, (int)T, d_model, H * dv, d_model, ws + m.blas, st);
   if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
   return retention_fail_(RET_OK, "");
 }
