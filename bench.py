@@ -195,7 +195,7 @@ def bench_parallel(steps, warmup):
     return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / BF16_PEAK_TFLOPS, "traffic": _read_traffic("parallel_2k"),
-                         "kernel": "qblock_kernel<256,512,parallel,split>",
+                         "kernel": "qblock_kernel<256,512,parallel> (hi+lo scores for the first query block of each sequence, bf16 for the rest)",
                          "algorithmic_tflop_per_call": flops / 1e12}}
 
 

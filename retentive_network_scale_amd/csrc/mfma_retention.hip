@@ -331,6 +331,9 @@ struct TileIO {
 struct TaskGeom {
   int nseg, seg_chunks, nsplit, nqb, ntasks;
   int nchunks;  // chunks per (b, h)
+  // query-block kernel task selection: 0 every query block; 1 only the first
+  // query block of each sequence (one task per (b, h)); 2 all but those
+  int sel = 0;
 };
 
 // XCD-aware task order: workgroup ids are dealt round-robin to the 8 XCDs, so
@@ -498,9 +501,16 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   const int task = xcd_task(blockIdx.x, geo.ntasks);
   if (task < 0) return;
   // task order: (bh, chunk, qb) with qb fastest; longest query blocks first
-  const int qb = geo.nqb - 1 - task % geo.nqb;
-  const int c = (task / geo.nqb) % geo.nchunks;
-  const int bh = task / (geo.nqb * geo.nchunks);
+  int qb = geo.nqb - 1 - task % geo.nqb;
+  int c = (task / geo.nqb) % geo.nchunks;
+  int bh = task / (geo.nqb * geo.nchunks);
+  if (geo.sel == 1) {
+    qb = 0;
+    c = 0;
+    bh = task;
+  } else if (geo.sel == 2 && qb == 0 && c == 0) {
+    return;
+  }
   const int cstep = PAR ? a.L : a.chunk;
   const int c0 = c * cstep, Cc = min(cstep, a.L - c0);
   const int q0 = c0 + qb * BT;
@@ -1083,14 +1093,28 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
   geo.nchunks = par ? 1 : (a.L + a.chunk - 1) / a.chunk;
   geo.ntasks = a.B * a.H * geo.nchunks * geo.nqb;
   const dim3 grid(xcd_grid(geo.ntasks));
-  if (par && a.use_gn)
-    hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid, dim3(NT), 0, st, a, geo, sinT, locT);
-  else if (par)
+  if (a.use_gn) {
+    // Under GroupNorm a row whose output variance is near eps is divided by
+    // about sqrt(eps), which magnifies bf16 score rounding: the first query block
+    // of a sequence (the rows that sum the fewest terms) takes hi+lo scores, the
+    // others plain bf16 ones.
+    TaskGeom g1 = geo, g2 = geo;
+    g1.sel = 1;
+    g1.ntasks = a.B * a.H;
+    g2.sel = 2;
+    const dim3 grid1(xcd_grid(g1.ntasks));
+    if (par) {
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid1, dim3(NT), 0, st, a, g1, sinT, locT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, g2, sinT, locT);
+    } else {
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid1, dim3(NT), 0, st, a, g1, sinT, locT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, g2, sinT, locT);
+    }
+  } else if (par) {
     hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, sinT, locT);
-  else if (a.use_gn)
-    hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid, dim3(NT), 0, st, a, geo, sinT, locT);
-  else
+  } else {
     hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, sinT, locT);
+  }
   return hipGetLastError();
 }
 
