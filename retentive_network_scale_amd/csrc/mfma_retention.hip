@@ -1093,11 +1093,12 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
   geo.nchunks = par ? 1 : (a.L + a.chunk - 1) / a.chunk;
   geo.ntasks = a.B * a.H * geo.nchunks * geo.nqb;
   const dim3 grid(xcd_grid(geo.ntasks));
-  if (a.use_gn) {
+  if (a.use_gn && a.use_theta) {
     // Under GroupNorm a row whose output variance is near eps is divided by
-    // about sqrt(eps), which magnifies bf16 score rounding: the first query block
-    // of a sequence (the rows that sum the fewest terms) takes hi+lo scores, the
-    // others plain bf16 ones.
+    // about sqrt(eps), which magnifies the rounding of the rotated q and k to
+    // bf16: the first query block of a sequence (the rows that sum the fewest
+    // terms) takes hi+lo scores, the others plain bf16 ones.  Without rotation
+    // the bf16 operands are the inputs themselves and their products are exact.
     TaskGeom g1 = geo, g2 = geo;
     g1.sel = 1;
     g1.ntasks = a.B * a.H;
@@ -1139,7 +1140,7 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
   if constexpr (IN_REGS) {
     geo.ntasks = a.B * a.H * geo.nseg;
     const dim3 grid(xcd_grid(geo.ntasks));
-    if (a.use_gn)
+    if (a.use_gn && a.use_theta)
       hipLaunchKernelGGL((seg_out_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, seg);
     else if (a.chunk <= KRES * BT)
       hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, true>), grid, dim3(NT), 0, st, a, geo, seg);
