@@ -316,6 +316,56 @@ def stats_summary(trace_dir, command):
         print(f"| `{name}` | {wg} | {vg} | {ag} | {sc} | {lds} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} |")
 
 
+MSR_DECODE_B, MSR_DECODE_STEPS = 64, 1024
+
+
+def bench_msr_decode(steps=MSR_DECODE_STEPS):
+    """Decode with the gated layer (d_model 2048, 8 heads, dk 256, dv 512) for 64
+    sequences: one captured msr_layer_step (positions advanced on the device)
+    replayed once per token.  The step's input rows stay in one static buffer;
+    every replay does the whole step's work."""
+    import torch
+    import retentive_network_scale_amd as rn
+    from workloads import MSR_LAYER as wl, randn
+    B = MSR_DECODE_B
+    _, wq, wk, wv, wg, wo = wl.inputs()
+    wd = [t.cuda() for t in (wq, wk, wv, wg, wo)]
+    g, th = wl.gamma(), wl.theta()
+    x = randn((B, wl.d_model), 5000, 1.0, torch.bfloat16).cuda()
+    y = torch.empty((B, wl.d_model), dtype=torch.bfloat16, device="cuda")
+    state = torch.zeros((B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(rn.msr_layer_step_workspace_bytes(B, wl.d_model, wl.H, wl.dk, wl.dv), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(adv):
+        rn.msr_layer_step(x, *wd, state, pos, wl.H, wl.dk, wl.dv, g, th, gn_eps=wl.gn_eps, advance_pos=adv,
+                          out=y, workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(True)
+    for _ in range(8):
+        graph.replay()
+    torch.cuda.synchronize()
+    t = _time_calls(graph.replay, steps, 0)
+    per_step = t / steps
+    weights = 2 * wl.d_model * (2 * wl.H * wl.dk + 3 * wl.H * wl.dv)
+    bytes_step = weights + 2 * 4 * B * wl.H * wl.dk * wl.dv + 2 * 2 * B * wl.d_model
+    achieved = bytes_step / per_step / 1e9
+    return {"tokens_per_s": B * steps / t, "ms_per_step": per_step * 1e3, "steps": steps, "batch": B,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "msr_layer_step graph replay (4 projection GEMMs, vec_step_kernel with "
+                                   "GroupNorm and gate, output GEMM, position advance)",
+                         "algorithmic_bytes_per_call": bytes_step}}
+
+
 def cpu_baseline(sample_tokens):
     """The fp64 oracle (chunkwise form, chunk 256) on the first `sample_tokens`
     tokens of all 8 heads of the long-context workload, timed on host cores."""
@@ -347,7 +397,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline chunkwise workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "msr", "sweep"],
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "msr", "msr_decode", "sweep"],
                     help="run one workload and print its figures (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the plain copy that calibrates the PMC byte counters")
@@ -380,6 +430,7 @@ def main():
         _log(args.only)
         res = {"decode": lambda: bench_decode(), "parallel": lambda: bench_parallel(args.steps, args.warmup),
                "msr": lambda: bench_msr(args.steps, args.warmup),
+               "msr_decode": lambda: bench_msr_decode(),
                "sweep": lambda: {"chunk_sweep": bench_chunk_sweep(args.steps, args.warmup)}}[args.only]()
         print(json.dumps({"workload": args.only, **res}), flush=True)
         return
@@ -402,6 +453,8 @@ def main():
         line["parallel"] = bench_parallel(max(3, args.steps // 2), args.warmup)
         _log("msr layer B4 L4096")
         line["msr_layer"] = bench_msr(max(3, args.steps // 4), args.warmup)
+        _log("msr decode B64, 1024 graph replays")
+        line["msr_decode"] = bench_msr_decode()
         _log("chunk-size sweep")
         line["chunk_sweep"] = bench_chunk_sweep(max(5, args.steps // 2), args.warmup)
     if not (args.no_cpu or args.only):

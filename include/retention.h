@@ -157,6 +157,32 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
                            const float *theta, long long pos0, float gn_eps, void *workspace,
                            size_t workspace_bytes, void *hip_stream);
 
+/*
+ * One decode step of the gated multi-scale retention layer (Sec. 2.2 with the
+ * recurrent representation, Sec. 2.1 (2); "RetNet dual-mode hands-on manual",
+ * Sec. 3.2 and 4.2: explicit per-sequence state, one token per step, replayed
+ * as a captured graph).  Every sequence b advances by one token x[b]:
+ *   q, k, v, g = x W_Q^T, x W_K^T, x W_V^T, x W_G^T   (per head: column blocks)
+ *   per head: S <- gamma_h S + k_rot^T v,  o = q_rot S   (rotation at pos[b])
+ *   y = (swish(g) (.) GroupNorm(o)) W_O^T
+ * so that steps over tokens 0..t-1 from a zero state reproduce msr_layer_fwd's
+ * outputs for those tokens (pos0 = 0).
+ *   x : [B, d_model] bf16      y : [B, d_model] bf16      weights as msr_layer_fwd
+ *   state : [B, H, dk, dv] fp32, DEVICE, read then overwritten in place
+ *   pos : DEVICE int32 [B], the position of this step's token per sequence; when
+ *         advance_pos != 0 the call adds 1 to every entry on the device after the
+ *         step, so a captured call can be replayed without host updates
+ * UNSUPPORTED unless d_model, H*dk and H*dv are multiples of 128, dk and dv are
+ * multiples of 8 and dv <= 1024.  y, state, x and the workspace must not overlap.
+ * The projections run through hipBLASLt as in msr_layer_fwd.
+ */
+size_t msr_layer_step_workspace_bytes(int B, int d_model, int H, int dk, int dv);
+ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, const void *w_v,
+                            const void *w_g, const void *w_o, void *y, float *state, int *pos,
+                            int advance_pos, int B, int d_model, int H, int dk, int dv,
+                            const float *gamma, const float *theta, float gn_eps, void *workspace,
+                            size_t workspace_bytes, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

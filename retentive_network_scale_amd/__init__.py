@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "RetentionError", "lib", "retention_parallel", "retention_chunkwise",
     "retention_chunkwise_workspace_bytes", "retention_recurrent_step", "msr_layer_fwd",
-    "msr_layer_fwd_workspace_bytes", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "msr_layer_fwd_workspace_bytes", "msr_layer_step", "msr_layer_step_workspace_bytes", "LIB_PATH",
+    "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libretention.so")
@@ -42,6 +43,9 @@ _SIGS = {
     "msr_layer_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "msr_layer_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _fp, _fp, _ll,
                            _f, _vp, _sz, _vp]),
+    "msr_layer_step_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "msr_layer_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _fp, _fp,
+                            _f, _vp, _sz, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -203,4 +207,32 @@ def msr_layer_fwd(x, w_q, w_k, w_v, w_g, w_o, H, dk, dv, chunk, gamma, theta=Non
     _check(lib().msr_layer_fwd(_dev(x, "x"), _dev(w_q, "w_q"), _dev(w_k, "w_k"), _dev(w_v, "w_v"),
                                _dev(w_g, "w_g"), _dev(w_o, "w_o"), _dev(out, "y"), B, L, dm, H, dk, dv,
                                int(chunk), gp, thp, int(pos0), float(gn_eps), ws, wsb, _stream(stream)))
+    return out
+
+
+def msr_layer_step_workspace_bytes(B, d_model, H, dk, dv):
+    return int(lib().msr_layer_step_workspace_bytes(B, d_model, H, dk, dv))
+
+
+def msr_layer_step(x, w_q, w_k, w_v, w_g, w_o, state, pos, H, dk, dv, gamma, theta=None, gn_eps=1e-5,
+                   advance_pos=True, out=None, workspace=None, stream=None):
+    """One decode step of the gated layer, bf16: x [B, d_model] (one token per
+    sequence), state [B, H, dk, dv] fp32 updated in place, pos int32 [B] on the
+    device (advanced by one on the device when advance_pos).  Weights as
+    msr_layer_fwd.  Returns y [B, d_model]."""
+    B, dm = x.shape
+    if out is None:
+        out = torch.empty((B, dm), dtype=torch.bfloat16, device=x.device)
+    need = msr_layer_step_workspace_bytes(B, dm, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if pos.dtype != torch.int32:
+        raise RetentionError(1, "pos must be int32")
+    g, gp = _host_f32(gamma, H, "gamma")
+    th, thp = _host_f32(theta, dk // 2, "theta")
+    _check(lib().msr_layer_step(_dev(x, "x"), _dev(w_q, "w_q"), _dev(w_k, "w_k"), _dev(w_v, "w_v"),
+                                _dev(w_g, "w_g"), _dev(w_o, "w_o"), _dev(out, "y"), _dev(state, "state"),
+                                _dev(pos, "pos"), int(bool(advance_pos)), B, dm, H, dk, dv, gp, thp,
+                                float(gn_eps), _dev(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
     return out

@@ -82,6 +82,12 @@ __device__ __forceinline__ float decay_pow(float g, float lg2, int d) {
 
 __device__ __forceinline__ float safe_log2(float g) { return g > 0.0f ? log2f(g) : -INFINITY; }
 
+// Gate multiplier from a gate value: swish(x) = x / (1 + e^-x) when `swish`
+// (the gated layer's swish(X W_G)), else x itself.
+__device__ __forceinline__ float gate_value(float x, int swish) {
+  return swish ? x / (1.0f + __expf(-x)) : x;
+}
+
 // ------------------------------------------------------------------ reductions
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -13,6 +13,8 @@ hipError_t launch_vec_parallel(const RetArgs &a, hipStream_t st);
 hipError_t launch_vec_chunkwise(const RetArgs &a, float *state_ws, const float *state_in,
                                 hipStream_t st);
 hipError_t launch_vec_step(const RetArgs &a, float *state, const int *pos, hipStream_t st);
+// pos[b] += 1 for b < B (device positions of decode steps)
+hipError_t launch_advance_pos(int *pos, int B, hipStream_t st);
 
 // MFMA kernels (bf16 inputs, supported (dk, dv) pairs only)
 bool mfma_supported(int dk, int dv);

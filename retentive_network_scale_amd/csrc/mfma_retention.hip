@@ -351,12 +351,6 @@ static inline unsigned xcd_grid(int ntasks) { return (unsigned)(((ntasks + 7) / 
 // Epilogue of a 64-query block held as O^T accumulators: optional GroupNorm over
 // all DV values of each (token, head) row (every wave holds RW of them), optional
 // bf16 gate multiply, store (bf16 or fp32) with the output strides of `a`.
-// Gate multiplier from a gate value: swish(x) = x / (1 + e^-x) when `swish`
-// (the gated layer's swish(X W_G)), else x itself.
-__device__ __forceinline__ float gate_value(float x, int swish) {
-  return swish ? x / (1.0f + __expf(-x)) : x;
-}
-
 // Column order of a wave's O^T rows.  With PAIR (two 16-row blocks per wave), row
 // m of block rb holds dv offset 8*(m/4) + 4*rb + m%4 of the wave's 32 columns, so
 // the D-layout accumulators of a lane -- rows 4g..4g+3 of both blocks -- are 8

@@ -176,4 +176,117 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
   return retention_fail_(RET_OK, "");
 }
 
+size_t msr_layer_step_workspace_bytes(int B, int d_model, int H, int dk, int dv) {
+  if (B <= 0 || d_model <= 0 || H <= 0 || dk <= 0 || dv <= 0) return 0;
+  const size_t NP = 2 * (size_t)H * dk + 2 * (size_t)H * dv;
+  return align256((size_t)B * NP * 2) + align256((size_t)B * H * dv * 2) + BLAS_WS;
+}
+
+// One decode step of the gated layer for B sequences (one token each):
+//   P = x [W_Q|W_K|W_V|W_G]^T (plain GEMMs), the recurrent retention step of every
+//   (sequence, head) at its position pos[b] on the caller's fp32 state, GroupNorm,
+//   the swish gate, then y = Z W_O^T; pos[b] += 1 on the device when advance_pos.
+ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, const void *w_v, const void *w_g,
+                            const void *w_o, void *y, float *state, int *pos, int advance_pos, int B, int d_model,
+                            int H, int dk, int dv, const float *gamma, const float *theta, float gn_eps,
+                            void *workspace, size_t workspace_bytes, void *hip_stream) {
+  if (B <= 0 || H <= 0 || d_model <= 0 || dk <= 0 || dv <= 0)
+    return retention_fail_(RET_ERR_INVALID_ARG, "sizes must be positive");
+  if (!gamma) return retention_fail_(RET_ERR_INVALID_ARG, "gamma is NULL");
+  if (H > RETENTION_MAX_HEADS || dk > RETENTION_MAX_DK || dv > RETENTION_MAX_DV)
+    return retention_fail_(RET_ERR_UNSUPPORTED, "too many heads or head size too large");
+  for (int h = 0; h < H; ++h)
+    if (!(gamma[h] >= 0.0f && gamma[h] <= 1.0f)) return retention_fail_(RET_ERR_INVALID_ARG, "gamma outside [0,1]");
+  if (theta) {
+    if (dk % 2) return retention_fail_(RET_ERR_INVALID_ARG, "rotation needs an even dk");
+    for (int i = 0; i < dk / 2; ++i)
+      if (!std::isfinite(theta[i])) return retention_fail_(RET_ERR_INVALID_ARG, "theta not finite");
+  }
+  if (!(gn_eps >= 0.0f) || !std::isfinite(gn_eps))
+    return retention_fail_(RET_ERR_INVALID_ARG, "gn_eps must be finite and >= 0 (the layer always normalises)");
+  if (d_model % 128 || (H * dk) % 128 || (H * dv) % 128 || dk % 8 || dv % 8)
+    return retention_fail_(RET_ERR_UNSUPPORTED, "d_model, H*dk and H*dv must be multiples of 128, dk and dv of 8");
+  if (dv / 4 > 256) return retention_fail_(RET_ERR_UNSUPPORTED, "dv too large for the step kernel");
+  if (!x || !w_q || !w_k || !w_v || !w_g || !w_o || !y || !state || !pos)
+    return retention_fail_(RET_ERR_INVALID_ARG, "NULL pointer");
+  const void *ptrs[] = {x, w_q, w_k, w_v, w_g, w_o, y, state, workspace};
+  for (const void *p : ptrs)
+    if ((uintptr_t)p & 15u) return retention_fail_(RET_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t need = msr_layer_step_workspace_bytes(B, d_model, H, dk, dv);
+  if (!workspace || workspace_bytes < need) return retention_fail_(RET_ERR_WORKSPACE, "workspace too small");
+  {
+    const uintptr_t y0 = (uintptr_t)y, y1 = y0 + (size_t)B * d_model * 2;
+    const uintptr_t s0 = (uintptr_t)state, s1 = s0 + (size_t)B * H * dk * dv * 4;
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need, x0 = (uintptr_t)x, x1 = x0 + (size_t)B * d_model * 2;
+    if ((y0 < w1 && w0 < y1) || (y0 < x1 && x0 < y1) || (y0 < s1 && s0 < y1) || (s0 < w1 && w0 < s1) ||
+        (s0 < x1 && x0 < s1))
+      return retention_fail_(RET_ERR_INVALID_ARG, "y, state, x and the workspace must not overlap");
+  }
+  hipStream_t st = (hipStream_t)hip_stream;
+  char *ws = (char *)workspace;
+  const long long NP = 2LL * H * dk + 2LL * H * dv;
+  uint16_t *proj = (uint16_t *)ws, *z = (uint16_t *)(ws + align256((size_t)B * NP * 2));
+  void *blas = ws + align256((size_t)B * NP * 2) + align256((size_t)B * H * dv * 2);
+  const long long cq = 0, ck = (long long)H * dk, cv = 2LL * H * dk, cg = cv + (long long)H * dv;
+
+  // 1. projections of this step's tokens into P[B][NP]
+  const uint16_t *X = (const uint16_t *)x;
+  const struct {
+    const void *w;
+    long long col;
+    int n;
+  } proj_w[4] = {{w_q, cq, H * dk}, {w_k, ck, H * dk}, {w_v, cv, H * dv}, {w_g, cg, H * dv}};
+  for (const auto &pw : proj_w) {
+    hipError_t e = plain_gemm(X, (const uint16_t *)pw.w, proj + pw.col, B, pw.n, d_model, (int)NP, blas, st);
+    if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  }
+
+  // 2. retention step with GroupNorm and the swish gate -> Z[B][H*dv]
+  RetArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = proj + cq;
+  a.k = proj + ck;
+  a.v = proj + cv;
+  a.o = z;
+  a.gate = proj + cg;
+  a.gate_swish = 1;
+  a.q_sb = NP;
+  a.q_sh = dk;
+  a.q_sn = dk;
+  a.v_sb = NP;
+  a.v_sh = dv;
+  a.v_sn = dv;
+  a.g_sb = NP;
+  a.g_sh = dv;
+  a.g_sn = dv;
+  a.o_sb = (long long)H * dv;
+  a.o_sh = dv;
+  a.o_sn = dv;
+  a.B = B;
+  a.H = H;
+  a.L = 1;
+  a.dk = dk;
+  a.dv = dv;
+  a.chunk = 1;
+  a.in_bf16 = 1;
+  a.out_bf16 = 1;
+  a.use_theta = theta != nullptr;
+  a.use_gn = 1;
+  a.gn_eps = gn_eps;
+  for (int h = 0; h < H; ++h) a.gamma[h] = gamma[h];
+  if (theta)
+    for (int i = 0; i < dk / 2; ++i) a.theta[i] = theta[i];
+  hipError_t e = launch_vec_step(a, state, pos, st);
+  if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+
+  // 3. output projection, 4. positions
+  e = plain_gemm(z, (const uint16_t *)w_o, (uint16_t *)y, B, d_model, H * dv, d_model, blas, st);
+  if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  if (advance_pos) {
+    e = launch_advance_pos(pos, B, st);
+    if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  }
+  return retention_fail_(RET_OK, "");
+}
+
 }  // extern "C"

@@ -49,8 +49,10 @@ __device__ __forceinline__ float score_vs_key(const RetArgs &a, const float *qro
   return s;
 }
 
-// GroupNorm over the dv columns spread as acc[c] <-> column threadIdx.x + c*VT, then store.
-__device__ __forceinline__ void gn_store(const RetArgs &a, float *acc, long long ooff, float *red) {
+// GroupNorm over the dv columns spread as acc[c] <-> column threadIdx.x + c*VT, then
+// the gate (when given; bf16 at element offset goff + column), then store.
+__device__ __forceinline__ void gn_store(const RetArgs &a, float *acc, long long ooff, float *red,
+                                         long long goff = 0) {
   const int t = threadIdx.x;
   if (a.use_gn) {
     float s = 0.0f;
@@ -67,6 +69,10 @@ __device__ __forceinline__ void gn_store(const RetArgs &a, float *acc, long long
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) acc[c] = (acc[c] - mean) * inv;
   }
+  if (a.gate)
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+      if (t + c * VT < a.dv) acc[c] *= gate_value(bf2f(a.gate[goff + t + c * VT]), a.gate_swish);
 #pragma unroll
   for (int c = 0; c < MAXC; ++c)
     if (t + c * VT < a.dv) store_elem(a.o, ooff + t + c * VT, acc[c], a.out_bf16);
@@ -294,7 +300,14 @@ __global__ __launch_bounds__(VT) void vec_step_kernel(RetArgs a, float *state, c
   float acc[MAXC];
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) acc[c] = (t + c * VT < a.dv) ? opart[t + c * VT] : 0.0f;
-  gn_store(a, acc, (long long)b * a.o_sb + (long long)h * a.o_sh, red);
+  gn_store(a, acc, (long long)b * a.o_sb + (long long)h * a.o_sh, red, (long long)b * a.g_sb + (long long)h * a.g_sh);
+}
+
+// Advances each sequence's position by one after a decode step (positions on the
+// device, so a captured step replays without host updates).
+__global__ void advance_pos_kernel(int *pos, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) pos[b] += 1;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -308,6 +321,11 @@ hipError_t launch_vec_parallel(const RetArgs &a, hipStream_t st) {
 hipError_t launch_vec_chunkwise(const RetArgs &a, float *state_ws, const float *state_in,
                                 hipStream_t st) {
   hipLaunchKernelGGL(vec_chunkwise_kernel, dim3(a.B * a.H), dim3(VT), 0, st, a, state_ws, state_in);
+  return hipGetLastError();
+}
+
+hipError_t launch_advance_pos(int *pos, int B, hipStream_t st) {
+  hipLaunchKernelGGL(advance_pos_kernel, dim3((B + 255) / 256), dim3(256), 0, st, pos, B);
   return hipGetLastError();
 }
 

@@ -115,3 +115,37 @@ def test_msr_rejects_unsupported_shapes():
     r = L.msr_layer_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, 1, 8, 40, 2, 24, 24, 8, g, None, 0,
                         1e-5, None, 0, None)
     assert r in (INVALID, UNSUPPORTED)
+
+
+def test_msr_step_rejects_and_workspace():
+    """Host-side validation of the decode step: every case fails before any launch."""
+    L = rn.lib()
+    g = _f([0.9] * 2)
+    INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+    need = L.msr_layer_step_workspace_bytes(4, 256, 2, 64, 128)
+    assert need >= 4 * (2 * 2 * 64 + 2 * 2 * 128) * 2 + 4 * 2 * 128 * 2
+    assert L.msr_layer_step_workspace_bytes(0, 256, 2, 64, 128) == 0
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, FAKE3, FAKE4, 1, 4, 256, 2, 64, 128, g, None, 1e-5]
+    # NULL state
+    a = list(args)
+    a[7] = None
+    assert L.msr_layer_step(*a, FAKE, need, None) == INVALID
+    # NULL positions
+    a = list(args)
+    a[8] = None
+    assert L.msr_layer_step(*a, FAKE, need, None) == INVALID
+    # gamma outside [0, 1]
+    a = list(args)
+    a[15] = _f([0.9, 1.5])
+    assert L.msr_layer_step(*a, FAKE, need, None) == INVALID
+    # d_model not a multiple of 128
+    a = list(args)
+    a[11] = 200
+    assert L.msr_layer_step(*a, FAKE, need, None) == UNSUPPORTED
+    # negative eps (the layer always normalises)
+    a = list(args)
+    a[17] = -1.0
+    assert L.msr_layer_step(*a, FAKE, need, None) == INVALID
+    # workspace too small
+    assert L.msr_layer_step(*args, FAKE, need - 1, None) == WORKSPACE
+    assert b"workspace" in L.retention_last_error()

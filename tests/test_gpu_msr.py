@@ -70,3 +70,93 @@ def test_msr_full_size_sampled():
                                gn_eps=wl.gn_eps, tokens=[(0, l) for l in ls])
         got = np.stack([yc[b, l] for l in ls])
         _tol.assert_bf16(got, ref, slice_dims=0, what=f"msr full-size batch {b}")
+
+
+def _step_weights(dm, H, dk, dv, seed, w_std=0.05):
+    bf = torch.bfloat16
+    return [randn((H * dk, dm), seed + 3, w_std, bf), randn((H * dk, dm), seed + 4, w_std, bf),
+            randn((H * dv, dm), seed + 5, w_std, bf), randn((H * dv, dm), seed + 6, w_std, bf),
+            randn((dm, H * dv), seed + 7, w_std, bf)]
+
+
+@pytest.mark.parametrize("B,T,dm,H,dk,dv", [(3, 24, 256, 2, 64, 128), (2, 10, 512, 2, 256, 512)])
+def test_msr_step_matches_layer(B, T, dm, H, dk, dv):
+    """Decode steps from a zero state reproduce the layer's outputs token by token
+    (the recurrent representation of the same layer), with a different starting
+    position per sequence."""
+    x = randn((B, T, dm), 800 + dk, 1.0, torch.bfloat16)
+    w = _step_weights(dm, H, dk, dv, 800 + dk)
+    g, th = multiscale_gamma(H), rotation_theta(dk)
+    starts = [0, 5, 11][:B]
+    wd = [t.to(DEV) for t in w]
+    state = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=DEV)
+    pos = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    ys = []
+    for t in range(T):
+        ys.append(rn.msr_layer_step(x[:, t].contiguous().to(DEV), *wd, state, pos, H, dk, dv, g, th, gn_eps=1e-5))
+    got = torch.stack(ys, 1)
+    torch.cuda.synchronize()
+    assert pos.cpu().tolist() == [s + T for s in starts]
+    for b in range(B):
+        ref = oracle.msr_layer(x[b:b + 1], *w, H, dk, dv, g, th, pos0=starts[b], gn_eps=1e-5)
+        _tol.assert_bf16(got[b:b + 1], ref, slice_dims=0, what=f"msr step b={b}")
+
+
+def test_msr_step_graph_replay():
+    """One step captured as a graph (positions advanced on the device) and replayed
+    once per token, with host copies and synchronisations between replays: every
+    replay equals the eager step."""
+    B, T, dm, H, dk, dv = 4, 12, 256, 2, 64, 128
+    x = randn((B, T, dm), 900, 1.0, torch.bfloat16).to(DEV)
+    wd = [t.to(DEV) for t in _step_weights(dm, H, dk, dv, 900)]
+    g, th = multiscale_gamma(H), rotation_theta(dk)
+    # eager reference
+    s_e = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=DEV)
+    p_e = torch.zeros(B, dtype=torch.int32, device=DEV)
+    eager = [rn.msr_layer_step(x[:, t].contiguous(), *wd, s_e, p_e, H, dk, dv, g, th) for t in range(T)]
+    # captured step on static buffers
+    xs = torch.empty((B, dm), dtype=torch.bfloat16, device=DEV)
+    ys = torch.empty((B, dm), dtype=torch.bfloat16, device=DEV)
+    s_g = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=DEV)
+    p_g = torch.zeros(B, dtype=torch.int32, device=DEV)
+    ws = torch.empty(rn.msr_layer_step_workspace_bytes(B, dm, H, dk, dv), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream (library plans are built here)
+        xs.copy_(x[:, 0])
+        rn.msr_layer_step(xs, *wd, s_g, p_g, H, dk, dv, g, th, out=ys, workspace=ws, advance_pos=False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    s_g.zero_()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rn.msr_layer_step(xs, *wd, s_g, p_g, H, dk, dv, g, th, out=ys, workspace=ws, advance_pos=True)
+    torch.cuda.synchronize()
+    s_g.zero_()
+    p_g.zero_()
+    torch.cuda.synchronize()
+    for t in range(T):
+        xs.copy_(x[:, t])
+        graph.replay()
+        torch.cuda.synchronize()
+        _tol.assert_bf16(ys, eager[t], slice_dims=0, what=f"replay {t}")
+    assert p_g.cpu().tolist() == [T] * B
+    _tol.assert_bf16(s_g, s_e, slice_dims=0, what="state after replays")
+
+
+def test_msr_step_full_layer_dims():
+    """The layer workload's dimensions (d_model 2048, 8 heads, dk 256, dv 512), 4
+    sequences, 6 steps from a zero state, against the oracle layer."""
+    wl = MSRWorkload()
+    B, T = 4, 6
+    x, wq, wk, wv, wg, wo = wl.inputs()
+    x = x[:, :T].contiguous()
+    g, th = wl.gamma(), wl.theta()
+    wd = [t.to(DEV) for t in (wq, wk, wv, wg, wo)]
+    state = torch.zeros((B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=DEV)
+    pos = torch.zeros(B, dtype=torch.int32, device=DEV)
+    got = torch.stack([rn.msr_layer_step(x[:, t].contiguous().to(DEV), *wd, state, pos, wl.H, wl.dk, wl.dv, g, th,
+                                         gn_eps=wl.gn_eps) for t in range(T)], 1)
+    torch.cuda.synchronize()
+    ref = oracle.msr_layer(x, wq, wk, wv, wg, wo, wl.H, wl.dk, wl.dv, g, th, pos0=0, gn_eps=wl.gn_eps)
+    _tol.assert_bf16(got, ref, slice_dims=0, what="msr step, layer dims")
