@@ -203,7 +203,9 @@ def bench_msr(steps, warmup):
     import torch
     import retentive_network_scale_amd as rn
     from workloads import MSR_LAYER as wl
-    x, wq, wk, wv, wg, wo = (t.cuda() for t in wl.inputs())
+    x, wq, wk, wv, wg, wo = wl.inputs()
+    x, wo = x.cuda(), wo.cuda()
+    wq, wk, wv, wg = _fused_qkvg(wq, wk, wv, wg)
     g, th = wl.gamma(), wl.theta()
     y = torch.empty((wl.B, wl.L, wl.d_model), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(rn.msr_layer_fwd_workspace_bytes(wl.B, wl.L, wl.d_model, wl.H, wl.dk, wl.dv, wl.chunk),
@@ -319,6 +321,15 @@ def stats_summary(trace_dir, command):
 MSR_DECODE_B, MSR_DECODE_STEPS = 64, 1024
 
 
+def _fused_qkvg(wq, wk, wv, wg):
+    """The four projection weights in one device buffer, rows [W_Q; W_K; W_V; W_G]
+    (as a model stores them), returned as views."""
+    import torch
+    cat = torch.cat([wq, wk, wv, wg], 0).cuda()
+    n = [wq.shape[0], wk.shape[0], wv.shape[0], wg.shape[0]]
+    return list(torch.split(cat, n, 0))
+
+
 def bench_msr_decode(steps=MSR_DECODE_STEPS):
     """Decode with the gated layer (d_model 2048, 8 heads, dk 256, dv 512) for 64
     sequences: one captured msr_layer_step (positions advanced on the device)
@@ -329,7 +340,7 @@ def bench_msr_decode(steps=MSR_DECODE_STEPS):
     from workloads import MSR_LAYER as wl, randn
     B = MSR_DECODE_B
     _, wq, wk, wv, wg, wo = wl.inputs()
-    wd = [t.cuda() for t in (wq, wk, wv, wg, wo)]
+    wd = [*_fused_qkvg(wq, wk, wv, wg), wo.cuda()]
     g, th = wl.gamma(), wl.theta()
     x = randn((B, wl.d_model), 5000, 1.0, torch.bfloat16).cuda()
     y = torch.empty((B, wl.d_model), dtype=torch.bfloat16, device="cuda")
@@ -361,7 +372,7 @@ def bench_msr_decode(steps=MSR_DECODE_STEPS):
     return {"tokens_per_s": B * steps / t, "ms_per_step": per_step * 1e3, "steps": steps, "batch": B,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "msr_layer_step graph replay (4 projection GEMMs, vec_step_kernel with "
+                         "kernel": "msr_layer_step graph replay (fused projection GEMM, vec_step_kernel with "
                                    "GroupNorm and gate, output GEMM, position advance)",
                          "algorithmic_bytes_per_call": bytes_step}}
 

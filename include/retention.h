@@ -143,7 +143,9 @@ ret_status_t retention_recurrent_step(const void *q, const void *k, const void *
  * UNSUPPORTED unless d_model, H*dk and H*dv are multiples of 128 and (dk, dv) is
  * one of the MFMA pairs listed under retention_parallel.
  * The four projections and W_O are plain GEMMs run through hipBLASLt (this
- * library's own GEMM kernel where hipBLASLt offers no algorithm); the first
+ * library's own GEMM kernel where hipBLASLt offers no algorithm).  When w_q,
+ * w_k, w_v and w_g are stored back to back in that order (one fused
+ * [2 H dk + 2 H dv, d_model] matrix), the projections run as one GEMM.  The first
  * call on a device creates that device's hipBLASLt handle, kept until the
  * process ends.  The workspace (size from msr_layer_fwd_workspace_bytes) holds
  * the projections [B*L][2 H dk + 2 H dv], the gated normalised heads

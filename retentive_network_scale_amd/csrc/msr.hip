@@ -62,6 +62,30 @@ hipError_t plain_gemm(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, 
   return launch_gemm_bf16(g, st);
 }
 
+// P[T][NP] = X [W_Q|W_K|W_V|W_G]^T.  When the four weights sit back to back in
+// memory (one [2 H dk + 2 H dv][K] matrix, rows in that order) this is a single
+// GEMM over all NP columns; otherwise one GEMM per weight.
+hipError_t projections(const uint16_t *X, const void *w_q, const void *w_k, const void *w_v, const void *w_g,
+                       uint16_t *P, int T, int K, int H, int dk, int dv, void *blas_ws, hipStream_t st) {
+  const long long NP = 2LL * H * dk + 2LL * H * dv;
+  const size_t qk_bytes = (size_t)H * dk * K * 2, vg_bytes = (size_t)H * dv * K * 2;
+  const char *q = (const char *)w_q;
+  if ((const char *)w_k == q + qk_bytes && (const char *)w_v == q + 2 * qk_bytes &&
+      (const char *)w_g == q + 2 * qk_bytes + vg_bytes)
+    return plain_gemm(X, (const uint16_t *)w_q, P, T, (int)NP, K, (int)NP, blas_ws, st);
+  const struct {
+    const void *w;
+    long long col;
+    int n;
+  } proj_w[4] = {{w_q, 0, H * dk}, {w_k, (long long)H * dk, H * dk}, {w_v, 2LL * H * dk, H * dv},
+                 {w_g, 2LL * H * dk + (long long)H * dv, H * dv}};
+  for (const auto &pw : proj_w) {
+    hipError_t e = plain_gemm(X, (const uint16_t *)pw.w, P + pw.col, T, pw.n, K, (int)NP, blas_ws, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 // Defined in abi.hip: records the message returned by retention_last_error().
@@ -118,15 +142,9 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
   const long long cq = 0, ck = (long long)H * dk, cv = 2LL * H * dk, cg = cv + (long long)H * dv;
 
   // 1. projections into P
-  const uint16_t *X = (const uint16_t *)x;
-  const struct {
-    const void *w;
-    long long col;
-    int n;
-  } proj_w[4] = {{w_q, cq, H * dk}, {w_k, ck, H * dk}, {w_v, cv, H * dv}, {w_g, cg, H * dv}};
-  for (const auto &pw : proj_w) {
-    hipError_t e = plain_gemm(X, (const uint16_t *)pw.w, proj + pw.col, (int)T, pw.n, d_model, (int)NP, ws + m.blas,
-                              st);
+  {
+    hipError_t e = projections((const uint16_t *)x, w_q, w_k, w_v, w_g, proj, (int)T, d_model, H, dk, dv,
+                               ws + m.blas, st);
     if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
   }
 
@@ -230,14 +248,8 @@ ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, con
   const long long cq = 0, ck = (long long)H * dk, cv = 2LL * H * dk, cg = cv + (long long)H * dv;
 
   // 1. projections of this step's tokens into P[B][NP]
-  const uint16_t *X = (const uint16_t *)x;
-  const struct {
-    const void *w;
-    long long col;
-    int n;
-  } proj_w[4] = {{w_q, cq, H * dk}, {w_k, ck, H * dk}, {w_v, cv, H * dv}, {w_g, cg, H * dv}};
-  for (const auto &pw : proj_w) {
-    hipError_t e = plain_gemm(X, (const uint16_t *)pw.w, proj + pw.col, B, pw.n, d_model, (int)NP, blas, st);
+  {
+    hipError_t e = projections((const uint16_t *)x, w_q, w_k, w_v, w_g, proj, B, d_model, H, dk, dv, blas, st);
     if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
   }
 

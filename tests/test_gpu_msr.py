@@ -160,3 +160,28 @@ def test_msr_step_full_layer_dims():
     torch.cuda.synchronize()
     ref = oracle.msr_layer(x, wq, wk, wv, wg, wo, wl.H, wl.dk, wl.dv, g, th, pos0=0, gn_eps=wl.gn_eps)
     _tol.assert_bf16(got, ref, slice_dims=0, what="msr step, layer dims")
+
+
+def test_msr_fused_weights_match_separate():
+    """Weights stored back to back (one fused projection matrix) take the
+    single-GEMM path; layer and step outputs match the separate-weight path and
+    the oracle."""
+    B, L, dm, H, dk, dv = 2, 96, 256, 2, 64, 128
+    x, (wq, wk, wv, wg, wo) = _inputs(B, L, dm, H, dk, dv, 950)
+    g, th = multiscale_gamma(H), rotation_theta(dk)
+    cat = torch.cat([wq, wk, wv, wg], 0).to(DEV)
+    fq, fk, fv, fg = torch.split(cat, [H * dk, H * dk, H * dv, H * dv], 0)
+    xd, wod = x.to(DEV), wo.to(DEV)
+    sep = [t.to(DEV) for t in (wq, wk, wv, wg)]
+    y_f = rn.msr_layer_fwd(xd, fq, fk, fv, fg, wod, H, dk, dv, 32, g, th, gn_eps=1e-5)
+    y_s = rn.msr_layer_fwd(xd, *sep, wod, H, dk, dv, 32, g, th, gn_eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.msr_layer(x, wq, wk, wv, wg, wo, H, dk, dv, g, th, pos0=0, gn_eps=1e-5)
+    _tol.assert_bf16(y_f, ref, slice_dims=0, what="fused weights, layer")
+    _tol.assert_bf16(y_f, y_s.float().cpu().double().numpy(), slice_dims=0, what="fused vs separate")
+    state = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=DEV)
+    pos = torch.zeros(B, dtype=torch.int32, device=DEV)
+    steps = torch.stack([rn.msr_layer_step(xd[:, t].contiguous(), fq, fk, fv, fg, wod, state, pos, H, dk, dv, g, th)
+                         for t in range(8)], 1)
+    torch.cuda.synchronize()
+    _tol.assert_bf16(steps, ref[:, :8], slice_dims=0, what="fused weights, steps")
