@@ -53,6 +53,8 @@ def _load():
         "orc_groupnorm": [_D, _l, _l, ctypes.c_double],
         "orc_matmul_nt": [_D, _D, _D, _l, _l, _l],
         "orc_swish": [_D, _l],
+        "orc_backward": [_D, _D, _D, _D, _l, _l, _l, _l, _l, _D, _D, _ll, _D, _D, _D],
+        "orc_backward_rows": [_D, _D, _D, _D, _l, _l, _l, _l, _l, _D, _D, _ll, ctypes.c_int, _L, _l, _D],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -166,6 +168,28 @@ def state_entries(k, v, gamma, idx, theta=None, pos0=0, s_in=None):
     s_in = as_f64(s_in)
     _load().orc_state_entries(_p(k), _p(v), B, H, L, dk, dv, _p(g), _p(_theta(theta)), pos0,
                               _p(s_in), ix.ctypes.data_as(_L), ix.shape[0], _p(out))
+    return out
+
+
+def backward(q, k, v, do, gamma, theta=None, pos0=0):
+    """Gradients (dq, dk, dv) of the defining sum (no GroupNorm) for output gradient do."""
+    q, k, v, do, g = as_f64(q), as_f64(k), as_f64(v), as_f64(do), as_f64(gamma)
+    B, H, L, dk, dv = _dims(q, v)
+    dq, dkk, dvv = np.empty((B, H, L, dk)), np.empty((B, H, L, dk)), np.empty((B, H, L, dv))
+    _load().orc_backward(_p(q), _p(k), _p(v), _p(do), B, H, L, dk, dv, _p(g), _p(_theta(theta)), pos0,
+                         _p(dq), _p(dkk), _p(dvv))
+    return dq, dkk, dvv
+
+
+def backward_rows(q, k, v, do, gamma, which, idx, theta=None, pos0=0):
+    """Rows of one gradient ('q', 'k' or 'v') at each (b, h, n) in idx."""
+    q, k, v, do, g = as_f64(q), as_f64(k), as_f64(v), as_f64(do), as_f64(gamma)
+    B, H, L, dk, dv = _dims(q, v)
+    w = {"q": 0, "k": 1, "v": 2}[which]
+    ix = np.ascontiguousarray(np.asarray(idx, dtype=np.int64).reshape(-1, 3))
+    out = np.empty((ix.shape[0], dv if w == 2 else dk))
+    _load().orc_backward_rows(_p(q), _p(k), _p(v), _p(do), B, H, L, dk, dv, _p(g), _p(_theta(theta)), pos0,
+                              w, ix.ctypes.data_as(_L), ix.shape[0], _p(out))
     return out
 
 

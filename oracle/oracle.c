@@ -256,6 +256,122 @@ void orc_rows(const double *q, const double *k, const double *v, long B, long H,
   }
 }
 
+/* The transpose of the rotation at position p: pair i multiplied by
+ * exp(-i p theta_i).  The rotation is orthogonal, so this is also its inverse. */
+static void unrotate_row(const double *x, long dk, long long p, const double *theta, double *out) {
+  if (!theta) {
+    memcpy(out, x, sizeof(double) * dk);
+    return;
+  }
+  for (long i = 0; i < dk / 2; ++i) {
+    double ang = (double)p * theta[i];
+    double c = cos(ang), s = sin(ang);
+    double re = x[2 * i], im = x[2 * i + 1];
+    out[2 * i] = re * c + im * s;
+    out[2 * i + 1] = -re * s + im * c;
+  }
+  if (dk & 1) out[dk - 1] = x[dk - 1];
+}
+
+/* Gradients of the defining sum (P2 Sec. 2.1, scalar-gamma form; no GroupNorm)
+ * with respect to q, k and v, for an output gradient dO.  With a_nm =
+ * gamma^(n-m) for n >= m and the rotated rows q~, k~:
+ *   dv_m  = sum_{n >= m} a_nm (q~_n . k~_m) dO_n
+ *   dq~_n = sum_{m <= n} a_nm (dO_n . v_m) k~_m,   dq_n = R_n^T dq~_n
+ *   dk~_m = sum_{n >= m} a_nm (dO_n . v_m) q~_n,   dk_m = R_m^T dk~_m
+ * (each term of o_n is bilinear in (q~_n, k~_m) and linear in v_m).  Written
+ * as one double loop over n >= m per (b, h). */
+void orc_backward(const double *q, const double *k, const double *v, const double *dO, long B, long H,
+                  long L, long dk, long dv, const double *gamma, const double *theta, long long pos0,
+                  double *dq, double *dkk, double *dvv) {
+#pragma omp parallel for schedule(dynamic)
+  for (long u = 0; u < B * H; ++u) {
+    long h = u % H;
+    double g = gamma[h];
+    double *qr = malloc(sizeof(double) * L * dk), *kr = malloc(sizeof(double) * L * dk);
+    double *dqr = calloc(L * dk, sizeof(double)), *dkr = calloc(L * dk, sizeof(double));
+    for (long n = 0; n < L; ++n) {
+      rotate_row(q + (u * L + n) * dk, dk, pos0 + n, theta, qr + n * dk);
+      rotate_row(k + (u * L + n) * dk, dk, pos0 + n, theta, kr + n * dk);
+    }
+    double *dvu = dvv + u * L * dv;
+    for (long i = 0; i < L * dv; ++i) dvu[i] = 0.0;
+    for (long n = 0; n < L; ++n) {
+      const double *don = dO + (u * L + n) * dv;
+      for (long m = 0; m <= n; ++m) {
+        double a = pow(g, (double)(n - m));
+        double s = dot(qr + n * dk, kr + m * dk, dk);
+        double t = dot(don, v + (u * L + m) * dv, dv);
+        for (long j = 0; j < dv; ++j) dvu[m * dv + j] += a * s * don[j];
+        for (long i = 0; i < dk; ++i) {
+          dqr[n * dk + i] += a * t * kr[m * dk + i];
+          dkr[m * dk + i] += a * t * qr[n * dk + i];
+        }
+      }
+    }
+    for (long n = 0; n < L; ++n) {
+      unrotate_row(dqr + n * dk, dk, pos0 + n, theta, dq + (u * L + n) * dk);
+      unrotate_row(dkr + n * dk, dk, pos0 + n, theta, dkk + (u * L + n) * dk);
+    }
+    free(qr);
+    free(kr);
+    free(dqr);
+    free(dkr);
+  }
+}
+
+/* Selected rows of the gradients above: which = 0 gives dq row n (a sum over
+ * m <= n), 1 gives dk row n and 2 gives dv row n (sums over later tokens).
+ * idx holds (b, h, n) triples; out receives dk values per row for which 0 and 1,
+ * dv values for which 2 (NaN for an index out of range). */
+void orc_backward_rows(const double *q, const double *k, const double *v, const double *dO, long B,
+                       long H, long L, long dk, long dv, const double *gamma, const double *theta,
+                       long long pos0, int which, const long *idx, long nidx, double *out) {
+  const long w = which == 2 ? dv : dk;
+#pragma omp parallel for schedule(dynamic)
+  for (long r = 0; r < nidx; ++r) {
+    long b = idx[3 * r], h = idx[3 * r + 1], n = idx[3 * r + 2];
+    double *o = out + r * w;
+    if (b < 0 || b >= B || h < 0 || h >= H || n < 0 || n >= L || which < 0 || which > 2) {
+      for (long j = 0; j < w; ++j) o[j] = NAN;
+      continue;
+    }
+    long u = b * H + h;
+    double g = gamma[h];
+    double *xr = malloc(sizeof(double) * dk), *yr = malloc(sizeof(double) * dk);
+    double *acc = calloc(w, sizeof(double));
+    if (which == 0) { /* dq~_n = sum_{m <= n} a_nm (dO_n . v_m) k~_m */
+      const double *don = dO + (u * L + n) * dv;
+      for (long m = 0; m <= n; ++m) {
+        rotate_row(k + (u * L + m) * dk, dk, pos0 + m, theta, xr);
+        double c = pow(g, (double)(n - m)) * dot(don, v + (u * L + m) * dv, dv);
+        for (long i = 0; i < dk; ++i) acc[i] += c * xr[i];
+      }
+      unrotate_row(acc, dk, pos0 + n, theta, o);
+    } else if (which == 1) { /* dk~_n = sum_{t >= n} a_tn (dO_t . v_n) q~_t */
+      const double *vn = v + (u * L + n) * dv;
+      for (long t = n; t < L; ++t) {
+        rotate_row(q + (u * L + t) * dk, dk, pos0 + t, theta, xr);
+        double c = pow(g, (double)(t - n)) * dot(dO + (u * L + t) * dv, vn, dv);
+        for (long i = 0; i < dk; ++i) acc[i] += c * xr[i];
+      }
+      unrotate_row(acc, dk, pos0 + n, theta, o);
+    } else { /* dv_n = sum_{t >= n} a_tn (q~_t . k~_n) dO_t */
+      rotate_row(k + (u * L + n) * dk, dk, pos0 + n, theta, yr);
+      for (long t = n; t < L; ++t) {
+        rotate_row(q + (u * L + t) * dk, dk, pos0 + t, theta, xr);
+        double c = pow(g, (double)(t - n)) * dot(xr, yr, dk);
+        const double *dot_ = dO + (u * L + t) * dv;
+        for (long j = 0; j < dv; ++j) acc[j] += c * dot_[j];
+      }
+      for (long j = 0; j < dv; ++j) o[j] = acc[j];
+    }
+    free(xr);
+    free(yr);
+    free(acc);
+  }
+}
+
 /* Selected entries of the state after all L tokens of a call: the recurrence
  * S_n = gamma S_{n-1} + k_n^T v_n (P2 Sec. 2.1 (2)) unrolled,
  *   S_L[a][b] = gamma^L S_in[a][b] + sum_m gamma^(L-1-m) k_m[a] v_m[b].
