@@ -122,6 +122,32 @@ def bench_chunkwise(steps, warmup):
     }
 
 
+def bench_chunkwise_bwd(steps, warmup):
+    """Gradients of retention (dq, dk, dv) on the long-context workload (B1 H8
+    L32768 dk128 dv256, chunk 256, bf16 in and out) for a seeded output gradient."""
+    import torch
+    import retentive_network_scale_amd as rn
+    from workloads import CHUNKWISE_32K as wl, randn
+    q, k, v = (t.cuda() for t in wl.qkv())
+    do = randn((wl.B, wl.H, wl.L, wl.dv), 3009, 1.0, torch.bfloat16).cuda()
+    g, th = wl.gamma(), wl.theta()
+    outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws = torch.empty(rn.retention_chunkwise_bwd_workspace_bytes(wl.B, wl.H, wl.L, wl.dk, wl.dv, wl.chunk),
+                     dtype=torch.uint8, device="cuda")
+    t = _time_calls(lambda: rn.retention_chunkwise_bwd(q, k, v, do, g, wl.chunk, th, out=outs, workspace=ws),
+                    steps, warmup)
+    per_call = t / steps
+    # algorithmic: q, k, v, dO read once; dq, dk, dv written once (bf16)
+    bytes_alg = 2 * wl.B * wl.H * wl.L * (2 * wl.dk + 2 * wl.dv) + 2 * wl.B * wl.H * wl.L * (2 * wl.dk + wl.dv)
+    achieved = bytes_alg / per_call / 1e9
+    return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "retention_chunkwise_bwd call: rotate/reverse passes, three chunkwise "
+                                   "retentions, un-rotate/reverse passes",
+                         "algorithmic_bytes_per_call": bytes_alg}}
+
+
 SWEEP_CHUNKS = (64, 128, 256, 512, 1024, 2048)
 
 
@@ -408,7 +434,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline chunkwise workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "msr", "msr_decode", "sweep"],
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "msr", "msr_decode", "sweep", "bwd"],
                     help="run one workload and print its figures (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the plain copy that calibrates the PMC byte counters")
@@ -442,6 +468,7 @@ def main():
         res = {"decode": lambda: bench_decode(), "parallel": lambda: bench_parallel(args.steps, args.warmup),
                "msr": lambda: bench_msr(args.steps, args.warmup),
                "msr_decode": lambda: bench_msr_decode(),
+               "bwd": lambda: bench_chunkwise_bwd(args.steps, args.warmup),
                "sweep": lambda: {"chunk_sweep": bench_chunk_sweep(args.steps, args.warmup)}}[args.only]()
         print(json.dumps({"workload": args.only, **res}), flush=True)
         return
@@ -464,6 +491,8 @@ def main():
         line["parallel"] = bench_parallel(max(3, args.steps // 2), args.warmup)
         _log("msr layer B4 L4096")
         line["msr_layer"] = bench_msr(max(3, args.steps // 4), args.warmup)
+        _log("chunkwise backward L=32768")
+        line["chunkwise_bwd"] = bench_chunkwise_bwd(max(3, args.steps // 4), args.warmup)
         _log("msr decode B64, 1024 graph replays")
         line["msr_decode"] = bench_msr_decode()
         _log("chunk-size sweep")

@@ -131,6 +131,31 @@ ret_status_t retention_recurrent_step(const void *q, const void *k, const void *
                                       void *hip_stream);
 
 /*
+ * Gradients of chunkwise retention (Sec. 2.1, no GroupNorm) with respect to q, k
+ * and v, for training ("RetNet dual-mode hands-on manual", Sec. 2.2: chunkwise
+ * mode for long-sequence training).  With a_nm = gamma^(n-m) for n >= m and the
+ * rotated rows q~, k~ of the forward call:
+ *   dv_m = sum_{n>=m} a_nm (q~_n . k~_m) dO_n
+ *   dq_n = R_n^T sum_{m<=n} a_nm (dO_n . v_m) k~_m
+ *   dk_m = R_m^T sum_{n>=m} a_nm (dO_n . v_m) q~_n
+ * (R_n: the rotation at position pos0 + n).  The initial state is zero.
+ * Each sum is itself a retention and runs on the chunkwise kernels with the given
+ * chunk (the two anti-causal sums on the token-reversed sequence).
+ *   q, k : [B,H,L,dk]   v, d_o : [B,H,L,dv]   (in_dtype)
+ *   dq, dk_out : [B,H,L,dk]   dv_out : [B,H,L,dv]   (out_dtype)
+ * UNSUPPORTED for odd dk or dv, or dv > RETENTION_MAX_DK.  Gradients must not
+ * overlap the inputs, the workspace or each other.
+ */
+size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int chunk,
+                                               ret_dtype_t in_dtype);
+ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v, const void *d_o,
+                                     void *dq, void *dk_out, void *dv_out, int B, int H, int L,
+                                     int dk, int dv, int chunk, const float *gamma,
+                                     const float *theta, long long pos0, ret_dtype_t in_dtype,
+                                     ret_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
+                                     void *hip_stream);
+
+/*
  * Gated multi-scale retention layer (Sec. 2.2), bf16 in and out:
  *   Q = X W_Q, K = X W_K, V = X W_V (head h = column block h of width dk / dv)
  *   head_h = chunkwise retention of (Q_h, K_h, V_h) with gamma_h, theta, pos0

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "RetentionError", "lib", "retention_parallel", "retention_chunkwise",
     "retention_chunkwise_workspace_bytes", "retention_recurrent_step", "msr_layer_fwd",
-    "msr_layer_fwd_workspace_bytes", "msr_layer_step", "msr_layer_step_workspace_bytes", "LIB_PATH",
+    "msr_layer_fwd_workspace_bytes", "msr_layer_step", "msr_layer_step_workspace_bytes",
+    "retention_chunkwise_bwd", "retention_chunkwise_bwd_workspace_bytes", "LIB_PATH",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -40,6 +41,9 @@ _SIGS = {
                                  _f, _i, _i, _vp, _sz, _vp]),
     "retention_recurrent_step": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _fp, _fp, _vp, _f, _i,
                                       _i, _vp]),
+    "retention_chunkwise_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "retention_chunkwise_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _fp, _fp, _ll,
+                                     _i, _i, _vp, _sz, _vp]),
     "msr_layer_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "msr_layer_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _fp, _fp, _ll,
                            _f, _vp, _sz, _vp]),
@@ -79,11 +83,15 @@ def _check(status):
 
 
 def _dt(t):
-    if t.dtype == torch.bfloat16:
+    return _dtc(t.dtype)
+
+
+def _dtc(dtype):
+    if dtype == torch.bfloat16:
         return RET_BF16
-    if t.dtype == torch.float32:
+    if dtype == torch.float32:
         return RET_F32
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    raise TypeError(f"unsupported dtype {dtype}")
 
 
 def _torch_dt(code):
@@ -235,4 +243,32 @@ def msr_layer_step(x, w_q, w_k, w_v, w_g, w_o, state, pos, H, dk, dv, gamma, the
                                 _dev(pos, "pos"), int(bool(advance_pos)), B, dm, H, dk, dv, gp, thp,
                                 float(gn_eps), _dev(workspace, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def retention_chunkwise_bwd_workspace_bytes(B, H, L, dk, dv, chunk, in_dtype=torch.bfloat16):
+    return int(lib().retention_chunkwise_bwd_workspace_bytes(B, H, L, dk, dv, chunk, _dtc(in_dtype)))
+
+
+def retention_chunkwise_bwd(q, k, v, d_o, gamma, chunk, theta=None, pos0=0, out_dtype=None, out=None,
+                            workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of chunkwise retention (no GroupNorm, zero initial
+    state) for the output gradient d_o.  q, k [B,H,L,dk]; v, d_o [B,H,L,dv]."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    od = out_dtype or q.dtype
+    if out is None:
+        out = (torch.empty((B, H, L, dk), dtype=od, device=q.device),
+               torch.empty((B, H, L, dk), dtype=od, device=q.device),
+               torch.empty((B, H, L, dv), dtype=od, device=q.device))
+    need = retention_chunkwise_bwd_workspace_bytes(B, H, L, dk, dv, chunk, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    g, gp = _host_f32(gamma, H, "gamma")
+    th, thp = _host_f32(theta, dk // 2, "theta")
+    _check(lib().retention_chunkwise_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(d_o, "d_o"),
+                                         _dev(out[0], "dq"), _dev(out[1], "dk"), _dev(out[2], "dv"), B, H, L, dk,
+                                         dv, int(chunk), gp, thp, int(pos0), _dtc(q.dtype), _dtc(od),
+                                         _dev(workspace, "workspace"),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out

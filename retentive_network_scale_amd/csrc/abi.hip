@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "retention.h"
@@ -127,6 +129,54 @@ bool use_mfma(int dk, int dv, ret_dtype_t in_dtype) {
 
 size_t vec_chunk_ws(int B, int H, int dk, int dv) { return (size_t)B * H * dk * dv * sizeof(float); }
 
+size_t chunk_ws_bytes(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_t in_dtype) {
+  return use_mfma(dk, dv, in_dtype) ? chunk_plan(B, H, L, dk, dv, chunk).ws_bytes : vec_chunk_ws(B, H, dk, dv);
+}
+
+// Backward workspace: rotated / reversed copies of the inputs (input dtype), the
+// three fp32 retention outputs and one chunkwise workspace shared by the three
+// retention calls (they run one after the other on the stream).
+struct BwdPlan {
+  size_t kr, krev, qrev, vrev, dorev, dq, dk, dv, cws, cws_bytes, total;
+};
+
+BwdPlan bwd_plan(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_t in_dtype) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t e = esize(in_dtype), R = (size_t)B * H * L;
+  BwdPlan p;
+  size_t off = 0;
+  p.kr = off;
+  off += al(R * dk * e);
+  p.krev = off;
+  off += al(R * dk * e);
+  p.qrev = off;
+  off += al(R * dk * e);
+  p.vrev = off;
+  off += al(R * dv * e);
+  p.dorev = off;
+  off += al(R * dv * e);
+  p.dq = off;
+  off += al(R * dk * 4);
+  p.dk = off;
+  off += al(R * dk * 4);
+  p.dv = off;
+  off += al(R * dv * 4);
+  p.cws = off;
+  p.cws_bytes = std::max(chunk_ws_bytes(B, H, L, dv, dk, chunk, in_dtype), chunk_ws_bytes(B, H, L, dk, dv, chunk, in_dtype));
+  off += al(p.cws_bytes);
+  p.total = off;
+  return p;
+}
+
+// One chunkwise retention of the backward: no rotation, no GroupNorm, fp32 output.
+hipError_t bwd_retention(const void *q, const void *k, const void *v, float *o, int B, int H, int L, int dqk,
+                         int dvv, int chunk, const float *gamma, ret_dtype_t in_dtype, void *cws, hipStream_t st) {
+  RetArgs a = make_args(q, k, v, o, B, H, L, dqk, dvv, chunk, gamma, nullptr, 0, -1.0f, in_dtype, RET_F32);
+  if (use_mfma(dqk, dvv, in_dtype))
+    return launch_mfma_chunkwise(a, chunk_plan(B, H, L, dqk, dvv, chunk), cws, nullptr, nullptr, st);
+  return launch_vec_chunkwise(a, (float *)cws, nullptr, st);
+}
+
 }  // namespace
 
 // Records the per-thread message of retention_last_error() for the other
@@ -228,6 +278,70 @@ ret_status_t retention_chunkwise(const void *q, const void *k, const void *v, vo
     S = (float *)workspace;
   }
   return hip_status(launch_vec_chunkwise(a, S, state_in, st));
+}
+
+size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_t in_dtype) {
+  if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+  return bwd_plan(B, H, L, dk, dv, chunk, in_dtype).total;
+}
+
+ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v, const void *d_o, void *dq,
+                                     void *dk_out, void *dv_out, int B, int H, int L, int dk, int dv, int chunk,
+                                     const float *gamma, const float *theta, long long pos0, ret_dtype_t in_dtype,
+                                     ret_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
+                                     void *hip_stream) {
+  ret_status_t s = check_common(B, H, L, dk, dv, gamma, theta, pos0, -1.0f, in_dtype, out_dtype);
+  if (s != RET_OK) return s;
+  if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk=%d must be positive", chunk);
+  if (dk % 2 || dv % 2) return fail(RET_ERR_UNSUPPORTED, "the backward needs even dk and dv");
+  if (dv > RETENTION_MAX_DK)  // dv is the query/key width of two of the inner retentions
+    return fail(RET_ERR_UNSUPPORTED, "the backward needs dv <= %d", RETENTION_MAX_DK);
+  if (L == 0) return ok();
+  if (!q || !k || !v || !d_o || !dq || !dk_out || !dv_out) return fail(RET_ERR_INVALID_ARG, "NULL tensor pointer");
+  const void *ptrs[] = {q, k, v, d_o, dq, dk_out, dv_out, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(RET_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const BwdPlan p = bwd_plan(B, H, L, dk, dv, chunk, in_dtype);
+  if (!workspace || workspace_bytes < p.total)
+    return fail(RET_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace_bytes);
+  const size_t R = (size_t)B * H * L;
+  const size_t nqk = R * dk * esize(in_dtype), nv = R * dv * esize(in_dtype);
+  const size_t oqk = R * dk * esize(out_dtype), ov = R * dv * esize(out_dtype);
+  const struct {
+    const void *p;
+    size_t n;
+  } ins[] = {{q, nqk}, {k, nqk}, {v, nv}, {d_o, nv}, {workspace, p.total}}, outs[] = {{dq, oqk}, {dk_out, oqk}, {dv_out, ov}};
+  for (const auto &o : outs) {
+    for (const auto &i : ins)
+      if (overlap(o.p, o.n, i.p, i.n)) return fail(RET_ERR_INVALID_ARG, "a gradient overlaps an input or the workspace");
+    for (const auto &o2 : outs)
+      if (o.p != o2.p && overlap(o.p, o.n, o2.p, o2.n)) return fail(RET_ERR_INVALID_ARG, "gradients overlap");
+  }
+  hipStream_t st = (hipStream_t)hip_stream;
+  char *ws = (char *)workspace;
+  RetArgs th = make_args(q, k, v, dq, B, H, L, dk, dv, chunk, gamma, theta, pos0, -1.0f, in_dtype, out_dtype);
+  const bool rot = theta != nullptr, bf = in_dtype == RET_BF16, obf = out_dtype == RET_BF16;
+  const long long rows = (long long)B * H * L;  // token rows of every tensor
+  hipError_t e;
+  // rotated keys (forward and reversed), rotated queries (reversed), reversed V and dO
+  if ((e = launch_bwd_prep(k, ws + p.kr, ws + p.krev, rows, L, dk, rot, pos0, bf, th, st)) != hipSuccess ||
+      (e = launch_bwd_prep(q, nullptr, ws + p.qrev, rows, L, dk, rot, pos0, bf, th, st)) != hipSuccess ||
+      (e = launch_bwd_prep(v, nullptr, ws + p.vrev, rows, L, dv, false, 0, bf, th, st)) != hipSuccess ||
+      (e = launch_bwd_prep(d_o, nullptr, ws + p.dorev, rows, L, dv, false, 0, bf, th, st)) != hipSuccess)
+    return hip_status(e);
+  float *dqr = (float *)(ws + p.dq), *dkr = (float *)(ws + p.dk), *dvr = (float *)(ws + p.dv);
+  void *cws = ws + p.cws;
+  if ((e = bwd_retention(d_o, v, ws + p.kr, dqr, B, H, L, dv, dk, chunk, gamma, in_dtype, cws, st)) != hipSuccess ||
+      (e = bwd_retention(ws + p.vrev, ws + p.dorev, ws + p.qrev, dkr, B, H, L, dv, dk, chunk, gamma, in_dtype, cws,
+                         st)) != hipSuccess ||
+      (e = bwd_retention(ws + p.krev, ws + p.qrev, ws + p.dorev, dvr, B, H, L, dk, dv, chunk, gamma, in_dtype, cws,
+                         st)) != hipSuccess)
+    return hip_status(e);
+  if ((e = launch_bwd_final(dqr, dq, rows, L, dk, false, rot, pos0, obf, th, st)) != hipSuccess ||
+      (e = launch_bwd_final(dkr, dk_out, rows, L, dk, true, rot, pos0, obf, th, st)) != hipSuccess ||
+      (e = launch_bwd_final(dvr, dv_out, rows, L, dv, true, false, 0, obf, th, st)) != hipSuccess)
+    return hip_status(e);
+  return ok();
 }
 
 ret_status_t retention_recurrent_step(const void *q, const void *k, const void *v, float *state,

@@ -13,6 +13,12 @@ hipError_t launch_vec_parallel(const RetArgs &a, hipStream_t st);
 hipError_t launch_vec_chunkwise(const RetArgs &a, float *state_ws, const float *state_in,
                                 hipStream_t st);
 hipError_t launch_vec_step(const RetArgs &a, float *state, const int *pos, hipStream_t st);
+// Backward passes (backward.hip): rotate and/or reverse the token order of a
+// [rows, L, d] tensor; un-rotate (and reverse) an fp32 gradient into out.
+hipError_t launch_bwd_prep(const void *x, void *dst_fwd, void *dst_rev, long long rows, int L, int d, bool rot,
+                           long long pos0, bool bf16, const RetArgs &th, hipStream_t st);
+hipError_t launch_bwd_final(const float *src, void *out, long long rows, int L, int d, bool rev, bool rot,
+                            long long pos0, bool out_bf16, const RetArgs &th, hipStream_t st);
 // pos[b] += 1 for b < B (device positions of decode steps)
 hipError_t launch_advance_pos(int *pos, int B, hipStream_t st);
 

@@ -1047,7 +1047,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, 
 // ---------------------------------------------------------------- dispatch
 bool mfma_supported(int dk, int dv) {
   return (dk == 64 && dv == 128) || (dk == 128 && dv == 128) || (dk == 128 && dv == 256) ||
-         (dk == 256 && dv == 256) || (dk == 256 && dv == 512);
+         (dk == 256 && dv == 128) || (dk == 256 && dv == 256) || (dk == 256 && dv == 512);
 }
 
 // dv columns per workgroup in the segment-state pass: the fp32 state slice
@@ -1136,8 +1136,8 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
     const dim3 grid(xcd_grid(geo.ntasks));
     if (a.use_gn && a.use_theta)
       hipLaunchKernelGGL((seg_out_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, seg);
-    else if (a.chunk <= KRES * BT)
-      hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, true>), grid, dim3(NT), 0, st, a, geo, seg);
+    else if (DK <= 128 && a.chunk <= KRES * BT)  // resident keys fit in LDS for DK <= 128
+      hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, (DK <= 128)>), grid, dim3(NT), 0, st, a, geo, seg);
     else
       hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, seg);
     return hipGetLastError();
@@ -1151,6 +1151,7 @@ hipError_t launch_mfma_parallel(const RetArgs &a, hipStream_t st) {
   if (a.dk == 64 && a.dv == 128) return run_qblocks<64, 128>(a, geo, true, nullptr, nullptr, st);
   if (a.dk == 128 && a.dv == 128) return run_qblocks<128, 128>(a, geo, true, nullptr, nullptr, st);
   if (a.dk == 128 && a.dv == 256) return run_qblocks<128, 256>(a, geo, true, nullptr, nullptr, st);
+  if (a.dk == 256 && a.dv == 128) return run_qblocks<256, 128>(a, geo, true, nullptr, nullptr, st);
   if (a.dk == 256 && a.dv == 256) return run_qblocks<256, 256>(a, geo, true, nullptr, nullptr, st);
   if (a.dk == 256 && a.dv == 512) return run_qblocks<256, 512>(a, geo, true, nullptr, nullptr, st);
   return hipErrorNotSupported;
@@ -1162,6 +1163,7 @@ hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &p, void *ws,
   if (a.dk == 64 && a.dv == 128) return run_chunkwise<64, 128>(a, p, w, state_in, state_out, st);
   if (a.dk == 128 && a.dv == 128) return run_chunkwise<128, 128>(a, p, w, state_in, state_out, st);
   if (a.dk == 128 && a.dv == 256) return run_chunkwise<128, 256>(a, p, w, state_in, state_out, st);
+  if (a.dk == 256 && a.dv == 128) return run_chunkwise<256, 128>(a, p, w, state_in, state_out, st);
   if (a.dk == 256 && a.dv == 256) return run_chunkwise<256, 256>(a, p, w, state_in, state_out, st);
   if (a.dk == 256 && a.dv == 512) return run_chunkwise<256, 512>(a, p, w, state_in, state_out, st);
   return hipErrorNotSupported;

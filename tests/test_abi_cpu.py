@@ -149,3 +149,22 @@ def test_msr_step_rejects_and_workspace():
     # workspace too small
     assert L.msr_layer_step(*args, FAKE, need - 1, None) == WORKSPACE
     assert b"workspace" in L.retention_last_error()
+
+
+def test_backward_rejects_and_workspace():
+    L = rn.lib()
+    g = _f([0.9] * 2)
+    INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+    need = L.retention_chunkwise_bwd_workspace_bytes(1, 2, 64, 16, 32, 16, 1)
+    assert need >= 3 * 2 * 64 * 16 * 2 + 2 * 2 * 64 * 32 * 2 + 4 * 2 * 64 * (16 + 16 + 32)
+    assert L.retention_chunkwise_bwd_workspace_bytes(1, 2, 0, 16, 32, 16, 1) == 0
+
+    def call(dk=16, dv=32, chunk=16, ws=FAKE4, wsb=need, dq=FAKE2, gamma=g):
+        return L.retention_chunkwise_bwd(FAKE, FAKE, FAKE, FAKE, dq, FAKE3, ctypes.c_void_p(0x500000), 1, 2, 64,
+                                         dk, dv, chunk, gamma, None, 0, 1, 1, ws, wsb, None)
+    assert call(dk=15) in (INVALID, UNSUPPORTED)
+    assert call(dv=1026) == UNSUPPORTED
+    assert call(chunk=0) == INVALID
+    assert call(gamma=_f([0.9, -0.1])) == INVALID
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(dq=FAKE) == INVALID  # a gradient overlapping an input
