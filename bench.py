@@ -144,7 +144,7 @@ def bench_chunkwise_bwd(steps, warmup):
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                          "kernel": "retention_chunkwise_bwd call: rotate/reverse passes, three chunkwise "
-                                   "retentions, un-rotate/reverse passes",
+                                   "retentions writing the gradients through an un-rotating, reversing epilogue",
                          "algorithmic_bytes_per_call": bytes_alg}}
 
 

@@ -143,7 +143,7 @@ ret_status_t retention_recurrent_step(const void *q, const void *k, const void *
  * chunk (the two anti-causal sums on the token-reversed sequence).
  *   q, k : [B,H,L,dk]   v, d_o : [B,H,L,dv]   (in_dtype)
  *   dq, dk_out : [B,H,L,dk]   dv_out : [B,H,L,dv]   (out_dtype)
- * UNSUPPORTED for odd dk or dv, or dv > RETENTION_MAX_DK.  Gradients must not
+ * UNSUPPORTED unless dk and dv are multiples of 8 and dv <= RETENTION_MAX_DK.  Gradients must not
  * overlap the inputs, the workspace or each other.
  */
 size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int chunk,

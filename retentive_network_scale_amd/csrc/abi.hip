@@ -168,13 +168,28 @@ BwdPlan bwd_plan(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_t in_
   return p;
 }
 
-// One chunkwise retention of the backward: no rotation, no GroupNorm, fp32 output.
-hipError_t bwd_retention(const void *q, const void *k, const void *v, float *o, int B, int H, int L, int dqk,
-                         int dvv, int chunk, const float *gamma, ret_dtype_t in_dtype, void *cws, hipStream_t st) {
-  RetArgs a = make_args(q, k, v, o, B, H, L, dqk, dvv, chunk, gamma, nullptr, 0, -1.0f, in_dtype, RET_F32);
-  if (use_mfma(dqk, dvv, in_dtype))
+// One chunkwise retention of the backward (no input rotation, no GroupNorm),
+// writing the gradient `out` directly: on the MFMA kernels the epilogue applies
+// the inverse rotation (out_rot) and the token reversal (out_rev); on the vector
+// path the result goes through fp32 scratch and a separate pass.
+hipError_t bwd_retention(const void *q, const void *k, const void *v, void *out, float *scratch, int B, int H, int L,
+                         int dqk, int dvv, int chunk, const float *gamma, const float *theta, long long pos0,
+                         bool out_rot, bool out_rev, ret_dtype_t in_dtype, ret_dtype_t out_dtype, void *cws,
+                         hipStream_t st) {
+  if (use_mfma(dqk, dvv, in_dtype)) {
+    RetArgs a = make_args(q, k, v, out, B, H, L, dqk, dvv, chunk, gamma, nullptr, pos0, -1.0f, in_dtype, out_dtype);
+    a.out_rev = out_rev;
+    a.out_rot = out_rot && theta;
+    if (a.out_rot)
+      for (int i = 0; i < dvv / 2; ++i) a.theta[i] = theta[i];
     return launch_mfma_chunkwise(a, chunk_plan(B, H, L, dqk, dvv, chunk), cws, nullptr, nullptr, st);
-  return launch_vec_chunkwise(a, (float *)cws, nullptr, st);
+  }
+  RetArgs a = make_args(q, k, v, scratch, B, H, L, dqk, dvv, chunk, gamma, nullptr, 0, -1.0f, in_dtype, RET_F32);
+  hipError_t e = launch_vec_chunkwise(a, (float *)cws, nullptr, st);
+  if (e != hipSuccess) return e;
+  RetArgs th = make_args(q, k, v, out, B, H, L, dvv, dvv, chunk, gamma, theta, pos0, -1.0f, in_dtype, out_dtype);
+  return launch_bwd_final(scratch, out, (long long)B * H * L, L, dvv, out_rev, out_rot && theta, pos0,
+                          out_dtype == RET_BF16, th, st);
 }
 
 }  // namespace
@@ -293,7 +308,7 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
   ret_status_t s = check_common(B, H, L, dk, dv, gamma, theta, pos0, -1.0f, in_dtype, out_dtype);
   if (s != RET_OK) return s;
   if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk=%d must be positive", chunk);
-  if (dk % 2 || dv % 2) return fail(RET_ERR_UNSUPPORTED, "the backward needs even dk and dv");
+  if (dk % 8 || dv % 8) return fail(RET_ERR_UNSUPPORTED, "the backward needs dk and dv multiples of 8");
   if (dv > RETENTION_MAX_DK)  // dv is the query/key width of two of the inner retentions
     return fail(RET_ERR_UNSUPPORTED, "the backward needs dv <= %d", RETENTION_MAX_DK);
   if (L == 0) return ok();
@@ -331,15 +346,12 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
     return hip_status(e);
   float *dqr = (float *)(ws + p.dq), *dkr = (float *)(ws + p.dk), *dvr = (float *)(ws + p.dv);
   void *cws = ws + p.cws;
-  if ((e = bwd_retention(d_o, v, ws + p.kr, dqr, B, H, L, dv, dk, chunk, gamma, in_dtype, cws, st)) != hipSuccess ||
-      (e = bwd_retention(ws + p.vrev, ws + p.dorev, ws + p.qrev, dkr, B, H, L, dv, dk, chunk, gamma, in_dtype, cws,
-                         st)) != hipSuccess ||
-      (e = bwd_retention(ws + p.krev, ws + p.qrev, ws + p.dorev, dvr, B, H, L, dk, dv, chunk, gamma, in_dtype, cws,
-                         st)) != hipSuccess)
-    return hip_status(e);
-  if ((e = launch_bwd_final(dqr, dq, rows, L, dk, false, rot, pos0, obf, th, st)) != hipSuccess ||
-      (e = launch_bwd_final(dkr, dk_out, rows, L, dk, true, rot, pos0, obf, th, st)) != hipSuccess ||
-      (e = launch_bwd_final(dvr, dv_out, rows, L, dv, true, false, 0, obf, th, st)) != hipSuccess)
+  if ((e = bwd_retention(d_o, v, ws + p.kr, dq, dqr, B, H, L, dv, dk, chunk, gamma, theta, pos0, true, false,
+                         in_dtype, out_dtype, cws, st)) != hipSuccess ||
+      (e = bwd_retention(ws + p.vrev, ws + p.dorev, ws + p.qrev, dk_out, dkr, B, H, L, dv, dk, chunk, gamma, theta,
+                         pos0, true, true, in_dtype, out_dtype, cws, st)) != hipSuccess ||
+      (e = bwd_retention(ws + p.krev, ws + p.qrev, ws + p.dorev, dv_out, dvr, B, H, L, dk, dv, chunk, gamma, nullptr,
+                         pos0, false, true, in_dtype, out_dtype, cws, st)) != hipSuccess)
     return hip_status(e);
   return ok();
 }

@@ -14,34 +14,57 @@
 
 namespace ret {
 
-// One thread per element pair (2i, 2i+1) of a token row of a [B*H, L, d] tensor;
-// rows = B*H*L, and token row r is position n = r % L of its sequence.
-// dst_fwd[n] = R_n x_n and dst_rev[L-1-n] = R_n x_n (R = identity unless rot).
-__global__ void bwd_prep_kernel(const void *x, void *dst_fwd, void *dst_rev, long long rows, int L, int d, int rot,
-                                long long pos0, int is_bf16, RetArgs th) {
+// One thread per 8 consecutive elements (4 pairs) of a token row of a
+// [B*H, L, d] tensor (d % 8 == 0); rows = B*H*L, token row r is position
+// n = r % L of its sequence.  dst_fwd[n] = R_n x_n and dst_rev[L-1-n] = R_n x_n
+// (R = identity unless rot; the angle is reduced in fp64 and the sine and cosine
+// taken in hardware, as the forward kernels do).
+template <typename E>
+__global__ void bwd_prep_kernel(const E *x, E *dst_fwd, E *dst_rev, long long rows, int L, int d, int rot,
+                                long long pos0, RetArgs th) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int pairs = d / 2;
-  if (i >= rows * pairs) return;
-  const long long row = i / pairs;
-  const int pr = (int)(i % pairs);
+  const int c8s = d / 8;
+  if (i >= rows * c8s) return;
+  const long long row = i / c8s;
+  const int c8 = (int)(i % c8s);
   const int n = (int)(row % L);
-  const long long off = row * d + 2 * pr;
-  float re = load_elem(x, off, is_bf16), im = load_elem(x, off + 1, is_bf16);
+  const long long off = row * d + 8 * c8;
+  float v[8];
+  if constexpr (sizeof(E) == 2) {
+    const uint4 raw = *(const uint4 *)(x + off);
+    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(wv[e] << 16);
+      v[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+    }
+  } else {
+    const float4 lo = *(const float4 *)(x + off), hi = *(const float4 *)(x + off + 4);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  }
   if (rot) {
-    float c, s;
-    rot_cs<true>(pos0 + n, th.theta[pr], c, s);
-    const float r2 = re * c - im * s, i2 = re * s + im * c;
-    re = r2;
-    im = i2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float c, sn;
+      rot_cs<false>(pos0 + n, th.theta[4 * c8 + j], c, sn);
+      const float re = v[2 * j], im = v[2 * j + 1];
+      v[2 * j] = re * c - im * sn;
+      v[2 * j + 1] = re * sn + im * c;
+    }
   }
-  if (dst_fwd) {
-    store_elem(dst_fwd, off, re, is_bf16);
-    store_elem(dst_fwd, off + 1, im, is_bf16);
-  }
-  if (dst_rev) {
-    const long long roff = (row - n + (L - 1 - n)) * d + 2 * pr;
-    store_elem(dst_rev, roff, re, is_bf16);
-    store_elem(dst_rev, roff + 1, im, is_bf16);
+  E *dsts[2] = {dst_fwd ? dst_fwd + off : nullptr,
+                dst_rev ? dst_rev + (row - n + (L - 1 - n)) * d + 8 * c8 : nullptr};
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (!dsts[t]) continue;
+    if constexpr (sizeof(E) == 2) {
+      *(uint4 *)dsts[t] = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                                     pack_bf2(v[6], v[7]));
+    } else {
+      *(float4 *)dsts[t] = make_float4(v[0], v[1], v[2], v[3]);
+      *(float4 *)(dsts[t] + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
   }
 }
 
@@ -69,9 +92,14 @@ __global__ void bwd_final_kernel(const float *src, void *out, long long rows, in
 
 hipError_t launch_bwd_prep(const void *x, void *dst_fwd, void *dst_rev, long long rows, int L, int d, bool rot,
                            long long pos0, bool bf16, const RetArgs &th, hipStream_t st) {
-  const long long n = rows * (d / 2);
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, dst_fwd, dst_rev,
-                     rows, L, d, (int)rot, pos0, (int)bf16, th);
+  const long long n = rows * (d / 8);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(bwd_prep_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)x, (uint16_t *)dst_fwd,
+                       (uint16_t *)dst_rev, rows, L, d, (int)rot, pos0, th);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<float>, grid, dim3(256), 0, st, (const float *)x, (float *)dst_fwd,
+                       (float *)dst_rev, rows, L, d, (int)rot, pos0, th);
   return hipGetLastError();
 }
 

@@ -19,6 +19,11 @@ struct RetArgs {
   void *o;
   const uint16_t *gate;  // optional bf16 multiplier applied after GroupNorm (gated layer)
   int gate_swish;        // the multiplier is swish(gate) = gate / (1 + exp(-gate)) instead of gate
+  // Output transforms of the MFMA epilogue (used by the backward): out_rev stores
+  // row n at L-1-n; out_rot multiplies output pair i of a row whose source token
+  // sits at position p by exp(-i p theta_i) (theta from this struct, p = pos0 +
+  // the row's index after any reversal).
+  int out_rev, out_rot;
   long long q_sb, q_sh, q_sn;
   long long v_sb, v_sh, v_sn;
   long long o_sb, o_sh, o_sn;

@@ -361,6 +361,20 @@ __device__ __forceinline__ int dv_of(int rb, int m) {
   return PAIR ? 8 * (m >> 2) + 4 * rb + (m & 3) : 16 * rb + m;
 }
 
+// out_rot of the epilogue: pairs (x[2j], x[2j+1]) of output columns pair0 + j
+// multiplied by exp(-i p theta) (the transpose of the rotation at position p).
+template <int N>
+__device__ __forceinline__ void unrotate_pairs(const RetArgs &a, float *x, long long p, int pair0) {
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j) {
+    float c, sn;
+    rot_cs<false>(p, a.theta[pair0 + j], c, sn);
+    const float re = x[2 * j], im = x[2 * j + 1];
+    x[2 * j] = re * c + im * sn;
+    x[2 * j + 1] = im * c - re * sn;
+  }
+}
+
 template <int RB, int RW, int DV, bool PAIR = false>
 __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB][4], float (*red)[BT], int b, int h,
                                                int q0, int nvalid, long long obase, int w, int g, int l16) {
@@ -411,10 +425,12 @@ __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB]
     for (int qb4 = 0; qb4 < 4; ++qb4) {
       const int r = 16 * qb4 + l16;
       if (r < nvalid) {
-        const long long ro = obase + (long long)(q0 + r) * a.o_sn;
+        const int n = a.out_rev ? a.L - 1 - (q0 + r) : q0 + r;
+        const long long ro = obase + (long long)n * a.o_sn;
         const int col = w * RW + 8 * g;
         float x[8] = {ot[0][qb4][0], ot[0][qb4][1], ot[0][qb4][2], ot[0][qb4][3],
                       ot[1][qb4][0], ot[1][qb4][1], ot[1][qb4][2], ot[1][qb4][3]};
+        if (a.out_rot) unrotate_pairs<8>(a, x, a.pos0 + n, col / 2);
         if (a.gate) {
           const long long go = (long long)b * a.g_sb + (long long)h * a.g_sh + (long long)(q0 + r) * a.g_sn + col;
           const u32x4 gg = *(const u32x4 *)(a.gate + go);
@@ -443,11 +459,17 @@ __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB]
   for (int qb4 = 0; qb4 < 4; ++qb4) {
     const int r = 16 * qb4 + l16;
     if (r < nvalid) {
-      const long long ro = obase + (long long)(q0 + r) * a.o_sn;
+      const int n = a.out_rev ? a.L - 1 - (q0 + r) : q0 + r;
+      const long long ro = obase + (long long)n * a.o_sn;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int col = w * RW + 16 * rb + 4 * g;
         f32x4 x = ot[rb][qb4];
+        if (a.out_rot) {
+          float xr[4] = {x[0], x[1], x[2], x[3]};
+          unrotate_pairs<4>(a, xr, a.pos0 + n, col / 2);
+          x = f32x4{xr[0], xr[1], xr[2], xr[3]};
+        }
         if (a.gate) {
           const long long go = (long long)b * a.g_sb + (long long)h * a.g_sh + (long long)(q0 + r) * a.g_sn + col;
           const u32x2 gg = *(const u32x2 *)(a.gate + go);
