@@ -53,6 +53,8 @@ def _load():
         "orc_groupnorm": [_D, _l, _l, ctypes.c_double],
         "orc_matmul_nt": [_D, _D, _D, _l, _l, _l],
         "orc_swish": [_D, _l],
+        "orc_layernorm": [_D, _l, _l, ctypes.c_double],
+        "orc_gelu": [_D, _l],
         "orc_backward": [_D, _D, _D, _D, _l, _l, _l, _l, _l, _D, _D, _ll, _D, _D, _D],
         "orc_backward_rows": [_D, _D, _D, _D, _l, _l, _l, _l, _l, _D, _D, _ll, ctypes.c_int, _L, _l, _D],
     }
@@ -216,6 +218,42 @@ def swish(x):
     x = as_f64(x).copy()
     _load().orc_swish(_p(x), x.size)
     return x
+
+
+def layernorm(x, eps):
+    """Per-row LayerNorm over the last axis, no affine."""
+    x = as_f64(x).copy()
+    _load().orc_layernorm(_p(x), x.size // x.shape[-1], x.shape[-1], float(eps))
+    return x
+
+
+def gelu(x):
+    """Exact gelu, x * Phi(x)."""
+    x = as_f64(x).copy()
+    _load().orc_gelu(_p(x), x.size)
+    return x
+
+
+def retnet_block(x, w_q, w_k, w_v, w_g, w_o, w_1, w_2, H, dk, dv, gamma, theta=None, pos0=0, gn_eps=1e-5,
+                 ln_eps=1e-5, tokens=None):
+    """The pre-LN residual block around the gated layer (P2, block equations):
+        Y = MSR(LN(X)) + X,   X' = FFN(LN(Y)) + Y,   FFN(Z) = gelu(Z W_1) W_2
+    with weights stored [out, in] (w_1 [d_ffn, d_model], w_2 [d_model, d_ffn]).
+    Returns [B, L, d_model], or only the rows in `tokens` ((b, l) pairs): every
+    step after the layer acts on one row at a time."""
+    x = as_f64(x)
+    B, L, dm = x.shape
+    h1 = layernorm(x, ln_eps)
+    if tokens is None:
+        y = msr_layer(h1, w_q, w_k, w_v, w_g, w_o, H, dk, dv, gamma, theta, pos0, gn_eps) + x
+        y = y.reshape(B * L, dm)
+    else:
+        toks = [tuple(t) for t in tokens]
+        y = msr_layer(h1, w_q, w_k, w_v, w_g, w_o, H, dk, dv, gamma, theta, pos0, gn_eps, tokens=toks)
+        y = y + np.stack([x[b, l] for b, l in toks])
+    f = matmul_nt(gelu(matmul_nt(layernorm(y, ln_eps), w_1)), w_2)
+    out = y + f
+    return out.reshape(B, L, dm) if tokens is None else out
 
 
 def msr_layer(x, w_q, w_k, w_v, w_g, w_o, H, dk, dv, gamma, theta=None, pos0=0, gn_eps=1e-5,

@@ -430,3 +430,26 @@ void orc_swish(double *x, long n) {
 #pragma omp parallel for schedule(static)
   for (long i = 0; i < n; ++i) x[i] = x[i] / (1.0 + exp(-x[i]));
 }
+
+/* LayerNorm of the block equations (P2, the pre-LN residual block): each row of
+ * d values becomes (x - mean) / sqrt(var + eps), biased variance, no affine
+ * parameters (the identity they start from).  In place. */
+void orc_layernorm(double *x, long rows, long d, double eps) {
+#pragma omp parallel for schedule(static)
+  for (long r = 0; r < rows; ++r) {
+    double *xr = x + r * d, mu = 0.0, var = 0.0;
+    for (long j = 0; j < d; ++j) mu += xr[j];
+    mu /= (double)d;
+    for (long j = 0; j < d; ++j) var += (xr[j] - mu) * (xr[j] - mu);
+    var /= (double)d;
+    double inv = 1.0 / sqrt(var + eps);
+    for (long j = 0; j < d; ++j) xr[j] = (xr[j] - mu) * inv;
+  }
+}
+
+/* gelu of the FFN (P2: FFN(X) = gelu(X W_1) W_2), the exact form
+ * x * Phi(x) = x (1 + erf(x / sqrt 2)) / 2.  In place. */
+void orc_gelu(double *x, long n) {
+#pragma omp parallel for schedule(static)
+  for (long i = 0; i < n; ++i) x[i] = 0.5 * x[i] * (1.0 + erf(x[i] / sqrt(2.0)));
+}
