@@ -344,6 +344,38 @@ def stats_summary(trace_dir, command):
         print(f"| `{name}` | {wg} | {vg} | {ag} | {sc} | {lds} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} |")
 
 
+def bench_block(steps, warmup):
+    """The pre-LN residual block around the gated layer at the layer workload's
+    dimensions, FFN width 2 d_model (the pages give none): one retnet_block_fwd."""
+    import torch
+    import retentive_network_scale_amd as rn
+    from workloads import MSR_LAYER as wl, randn
+    x, wq, wk, wv, wg, wo = wl.inputs()
+    dff = 2 * wl.d_model
+    w1 = randn((dff, wl.d_model), 5008, wl.w_std, torch.bfloat16).cuda()
+    w2 = randn((wl.d_model, dff), 5009, wl.w_std, torch.bfloat16).cuda()
+    x, wo = x.cuda(), wo.cuda()
+    wq, wk, wv, wg = _fused_qkvg(wq, wk, wv, wg)
+    g, th = wl.gamma(), wl.theta()
+    out = torch.empty_like(x)
+    ws = torch.empty(rn.retnet_block_fwd_workspace_bytes(wl.B, wl.L, wl.d_model, wl.H, wl.dk, wl.dv, dff,
+                                                         wl.chunk), dtype=torch.uint8, device="cuda")
+    t = _time_calls(lambda: rn.retnet_block_fwd(x, wq, wk, wv, wg, wo, w1, w2, wl.H, wl.dk, wl.dv, wl.chunk, g, th,
+                                                gn_eps=wl.gn_eps, out=out, workspace=ws), steps, warmup)
+    per_call = t / steps
+    T, C = wl.B * wl.L, wl.chunk
+    gemm = 2 * T * wl.d_model * (2 * wl.H * wl.dk + 2 * wl.H * wl.dv) + 2 * T * wl.H * wl.dv * wl.d_model
+    ret = T * wl.H * ((C + 1) * (wl.dk + wl.dv) + 4 * wl.dk * wl.dv)
+    ffn = 4 * T * wl.d_model * dff
+    tf = (gemm + ret + ffn) / per_call / 1e12
+    return {"tokens_per_s": T / per_call, "ms_per_step": per_call * 1e3, "d_ffn": dff,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                         "kernel": "retnet_block_fwd (LayerNorm, gated layer, residual GEMM, LayerNorm, FFN GEMMs "
+                                   "with gelu, residual GEMM)",
+                         "algorithmic_tflop_per_call": (gemm + ret + ffn) / 1e12}}
+
+
 MSR_DECODE_B, MSR_DECODE_STEPS = 64, 1024
 
 
@@ -434,7 +466,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline chunkwise workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "msr", "msr_decode", "sweep", "bwd"],
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "msr", "msr_decode", "sweep", "bwd",
+                                       "block"],
                     help="run one workload and print its figures (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the plain copy that calibrates the PMC byte counters")
@@ -469,6 +502,7 @@ def main():
                "msr": lambda: bench_msr(args.steps, args.warmup),
                "msr_decode": lambda: bench_msr_decode(),
                "bwd": lambda: bench_chunkwise_bwd(args.steps, args.warmup),
+               "block": lambda: bench_block(args.steps, args.warmup),
                "sweep": lambda: {"chunk_sweep": bench_chunk_sweep(args.steps, args.warmup)}}[args.only]()
         print(json.dumps({"workload": args.only, **res}), flush=True)
         return
@@ -491,6 +525,8 @@ def main():
         line["parallel"] = bench_parallel(max(3, args.steps // 2), args.warmup)
         _log("msr layer B4 L4096")
         line["msr_layer"] = bench_msr(max(3, args.steps // 4), args.warmup)
+        _log("retnet block B4 L4096")
+        line["retnet_block"] = bench_block(max(3, args.steps // 4), args.warmup)
         _log("chunkwise backward L=32768")
         line["chunkwise_bwd"] = bench_chunkwise_bwd(max(3, args.steps // 4), args.warmup)
         _log("msr decode B64, 1024 graph replays")

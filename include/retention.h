@@ -210,6 +210,26 @@ ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, con
                             const float *gamma, const float *theta, float gn_eps, void *workspace,
                             size_t workspace_bytes, void *hip_stream);
 
+/*
+ * The pre-LN residual block around the gated layer (paper summary, the block
+ * equations; FFN(X) = gelu(X W_1) W_2), bf16 in and out:
+ *   Y = MSR(LN(X)) + X,   out = FFN(LN(Y)) + Y
+ * LN: per token over d_model, (x - mean) / sqrt(var + ln_eps), biased variance,
+ * no affine; gelu(x) = x Phi(x) (the exact form).  MSR as msr_layer_fwd.
+ *   w_1 : [d_ffn, d_model] bf16   w_2 : [d_model, d_ffn] bf16   (stored [out, in])
+ * UNSUPPORTED unless d_model, H*dk, H*dv and d_ffn are multiples of 128,
+ * d_model <= 8192 and (dk, dv) is an MFMA pair.  out must not overlap x or the
+ * workspace.  GEMMs run through hipBLASLt as in msr_layer_fwd.
+ */
+size_t retnet_block_fwd_workspace_bytes(int B, int L, int d_model, int H, int dk, int dv, int d_ffn,
+                                        int chunk);
+ret_status_t retnet_block_fwd(const void *x, const void *w_q, const void *w_k, const void *w_v,
+                              const void *w_g, const void *w_o, const void *w_1, const void *w_2,
+                              void *out, int B, int L, int d_model, int H, int dk, int dv, int d_ffn,
+                              int chunk, const float *gamma, const float *theta, long long pos0,
+                              float gn_eps, float ln_eps, void *workspace, size_t workspace_bytes,
+                              void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

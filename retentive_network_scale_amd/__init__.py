@@ -18,7 +18,8 @@ __all__ = [
     "RetentionError", "lib", "retention_parallel", "retention_chunkwise",
     "retention_chunkwise_workspace_bytes", "retention_recurrent_step", "msr_layer_fwd",
     "msr_layer_fwd_workspace_bytes", "msr_layer_step", "msr_layer_step_workspace_bytes",
-    "retention_chunkwise_bwd", "retention_chunkwise_bwd_workspace_bytes", "LIB_PATH",
+    "retention_chunkwise_bwd", "retention_chunkwise_bwd_workspace_bytes", "retnet_block_fwd",
+    "retnet_block_fwd_workspace_bytes", "LIB_PATH",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -48,6 +49,9 @@ _SIGS = {
     "msr_layer_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _fp, _fp, _ll,
                            _f, _vp, _sz, _vp]),
     "msr_layer_step_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "retnet_block_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "retnet_block_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _fp,
+                              _fp, _ll, _f, _f, _vp, _sz, _vp]),
     "msr_layer_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _fp, _fp,
                             _f, _vp, _sz, _vp]),
 }
@@ -271,4 +275,29 @@ def retention_chunkwise_bwd(q, k, v, d_o, gamma, chunk, theta=None, pos0=0, out_
                                          dv, int(chunk), gp, thp, int(pos0), _dtc(q.dtype), _dtc(od),
                                          _dev(workspace, "workspace"),
                                          workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def retnet_block_fwd_workspace_bytes(B, L, d_model, H, dk, dv, d_ffn, chunk):
+    return int(lib().retnet_block_fwd_workspace_bytes(B, L, d_model, H, dk, dv, d_ffn, chunk))
+
+
+def retnet_block_fwd(x, w_q, w_k, w_v, w_g, w_o, w_1, w_2, H, dk, dv, chunk, gamma, theta=None, pos0=0,
+                     gn_eps=1e-5, ln_eps=1e-5, out=None, workspace=None, stream=None):
+    """Pre-LN residual block: Y = MSR(LN(x)) + x, out = gelu(LN(Y) W_1^T) W_2^T + Y (bf16).
+    Weights stored [out, in]; w_1 [d_ffn, d_model], w_2 [d_model, d_ffn]."""
+    B, L, dm = x.shape
+    dff = w_1.shape[0]
+    if out is None:
+        out = torch.empty((B, L, dm), dtype=torch.bfloat16, device=x.device)
+    need = retnet_block_fwd_workspace_bytes(B, L, dm, H, dk, dv, dff, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    g, gp = _host_f32(gamma, H, "gamma")
+    th, thp = _host_f32(theta, dk // 2, "theta")
+    _check(lib().retnet_block_fwd(_dev(x, "x"), _dev(w_q, "w_q"), _dev(w_k, "w_k"), _dev(w_v, "w_v"),
+                                  _dev(w_g, "w_g"), _dev(w_o, "w_o"), _dev(w_1, "w_1"), _dev(w_2, "w_2"),
+                                  _dev(out, "out"), B, L, dm, H, dk, dv, dff, int(chunk), gp, thp, int(pos0),
+                                  float(gn_eps), float(ln_eps), _dev(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
     return out

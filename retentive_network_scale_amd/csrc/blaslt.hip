@@ -1,11 +1,13 @@
-// Plain bf16 GEMMs of the gated layer's projections ("Retentive Network" paper
-// summary, Sec. 2.2: X W_Q, X W_K, X W_V, X W_G and the output projection) through
-// hipBLASLt.  These products carry no fused arithmetic -- the layer reads its
-// operands back through strides and applies swish in the retention epilogue -- so
-// a library GEMM is used for them; everything specific to retention runs in this
-// library's own kernels.
+// Plain bf16 GEMMs through hipBLASLt: the gated layer's projections ("Retentive
+// Network" paper summary, Sec. 2.2: X W_Q, X W_K, X W_V, X W_G and the output
+// projection) and the block's FFN (gelu(X W_1) W_2).  These products carry no
+// fused arithmetic beyond a residual add -- the layer reads its operands back
+// through strides and applies swish in the retention epilogue -- so a library GEMM
+// is used for them; everything specific to retention runs in this library's own
+// kernels.
 //
-//   C[t][n] = sum_k X[t][k] W[n][k]     (row-major, bf16 in and out, fp32 accumulate)
+//   C[t][n] = sum_k X[t][k] W[n][k] (+ R[t][n])   (row-major, bf16 in and out,
+//                                                  fp32 accumulate; R optional)
 //
 // In hipBLASLt's column-major terms this is C^T (N x T, ld ldc) = W (N x K) * X^T
 // (K x T), with W given as its stored K x N column-major transpose: a "TN" product.
@@ -82,16 +84,16 @@ const Plan *get_plan(int dev, hipblasLtHandle_t *handle, int T, int N, int K, in
 }  // namespace
 
 hipError_t blaslt_gemm_nt(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, int N, int K, int ldc,
-                          void *ws, size_t ws_bytes, hipStream_t st) {
+                          void *ws, size_t ws_bytes, hipStream_t st, const uint16_t *R) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   hipblasLtHandle_t handle = nullptr;
   const Plan *p = get_plan(dev, &handle, T, N, K, ldc, ws_bytes);
   if (!p) return hipErrorNotSupported;
-  const float alpha = 1.0f, beta = 0.0f;
-  const hipblasStatus_t s = hipblasLtMatmul(handle, p->desc, &alpha, W, p->la, X, p->lb, &beta, C, p->lc, C,
-                                            p->lc, &p->algo, p->ws ? ws : nullptr, p->ws, st);
+  const float alpha = 1.0f, beta = R ? 1.0f : 0.0f;
+  const hipblasStatus_t s = hipblasLtMatmul(handle, p->desc, &alpha, W, p->la, X, p->lb, &beta, R ? R : C, p->lc,
+                                            C, p->lc, &p->algo, p->ws ? ws : nullptr, p->ws, st);
   return s == HIPBLAS_STATUS_SUCCESS ? hipSuccess : hipErrorLaunchFailure;
 }
 

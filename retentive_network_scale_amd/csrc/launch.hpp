@@ -60,9 +60,16 @@ struct GemmArgs {
 hipError_t launch_gemm_bf16(const GemmArgs &args, hipStream_t st);
 
 // Plain bf16 GEMM through hipBLASLt (blaslt.hip): C[t][n] = sum_k X[t][k] W[n][k]
-// for t < T, n < N, row-major with row stride ldc.  hipErrorNotSupported when
-// hipBLASLt has no algorithm for the shape within ws_bytes of workspace.
+// (+ R[t][n] when R is given, same layout as C) for t < T, n < N, row-major with
+// row stride ldc.  hipErrorNotSupported when hipBLASLt has no algorithm for the
+// shape within ws_bytes of workspace.
 hipError_t blaslt_gemm_nt(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, int N, int K, int ldc,
-                          void *ws, size_t ws_bytes, hipStream_t st);
+                          void *ws, size_t ws_bytes, hipStream_t st, const uint16_t *R = nullptr);
+
+// Row-wise bf16 passes of the residual block (block.hip): LayerNorm without
+// affine (y may alias x), exact gelu in place, and c += r.
+hipError_t launch_layernorm_bf16(const uint16_t *x, uint16_t *y, long long rows, int d, float eps, hipStream_t st);
+hipError_t launch_gelu_bf16(uint16_t *x, long long n, hipStream_t st);
+hipError_t launch_add_bf16(uint16_t *c, const uint16_t *r, long long n, hipStream_t st);
 
 }  // namespace ret

@@ -47,10 +47,11 @@ MsrLayout msr_layout(int B, int L, int H, int dk, int dv, int chunk) {
   return m;
 }
 
-// C[t][n] = sum_k X[t][k] W[n][k] (row stride ldc): hipBLASLt, else this library's GEMM kernel.
+// C[t][n] = sum_k X[t][k] W[n][k] (+ R[t][n]) (row stride ldc): hipBLASLt, else
+// this library's GEMM kernel (and a separate add for R, which then has ldc == N).
 hipError_t plain_gemm(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, int N, int K, int ldc, void *blas_ws,
-                      hipStream_t st) {
-  hipError_t e = blaslt_gemm_nt(X, W, C, T, N, K, ldc, blas_ws, BLAS_WS, st);
+                      hipStream_t st, const uint16_t *R = nullptr) {
+  hipError_t e = blaslt_gemm_nt(X, W, C, T, N, K, ldc, blas_ws, BLAS_WS, st, R);
   if (e != hipErrorNotSupported) return e;
   GemmArgs g;
   memset(&g, 0, sizeof(g));
@@ -59,7 +60,9 @@ hipError_t plain_gemm(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, 
   g.K = K;
   g.nseg = 1;
   g.seg[0] = GemmSeg{W, N, GEMM_PLAIN, C, (long long)ldc, 0, 0, 0};
-  return launch_gemm_bf16(g, st);
+  e = launch_gemm_bf16(g, st);
+  if (e != hipSuccess || !R) return e;
+  return launch_add_bf16(C, R, (long long)T * N, st);
 }
 
 // P[T][NP] = X [W_Q|W_K|W_V|W_G]^T.  When the four weights sit back to back in
@@ -91,52 +94,12 @@ hipError_t projections(const uint16_t *X, const void *w_q, const void *w_k, cons
 // Defined in abi.hip: records the message returned by retention_last_error().
 ret_status_t retention_fail_(ret_status_t s, const char *msg);
 
-extern "C" {
-
-size_t msr_layer_fwd_workspace_bytes(int B, int L, int d_model, int H, int dk, int dv, int chunk) {
-  if (B <= 0 || L <= 0 || d_model <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
-  if (!mfma_supported(dk, dv)) return 0;
-  return msr_layout(B, L, H, dk, dv, chunk).total;
-}
-
-ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, const void *w_v, const void *w_g,
-                           const void *w_o, void *y, int B, int L, int d_model, int H, int dk, int dv, int chunk,
-                           const float *gamma, const float *theta, long long pos0, float gn_eps, void *workspace,
-                           size_t workspace_bytes, void *hip_stream) {
-  if (B <= 0 || H <= 0 || L < 0 || d_model <= 0 || dk <= 0 || dv <= 0 || chunk <= 0)
-    return retention_fail_(RET_ERR_INVALID_ARG, "sizes must be positive");
-  if (!gamma) return retention_fail_(RET_ERR_INVALID_ARG, "gamma is NULL");
-  if (H > RETENTION_MAX_HEADS) return retention_fail_(RET_ERR_UNSUPPORTED, "too many heads");
-  for (int h = 0; h < H; ++h)
-    if (!(gamma[h] >= 0.0f && gamma[h] <= 1.0f)) return retention_fail_(RET_ERR_INVALID_ARG, "gamma outside [0,1]");
-  if (theta) {
-    if (dk % 2) return retention_fail_(RET_ERR_INVALID_ARG, "rotation needs an even dk");
-    for (int i = 0; i < dk / 2; ++i)
-      if (!std::isfinite(theta[i])) return retention_fail_(RET_ERR_INVALID_ARG, "theta not finite");
-  }
-  if (!(gn_eps >= 0.0f) || !std::isfinite(gn_eps))
-    return retention_fail_(RET_ERR_INVALID_ARG, "gn_eps must be finite and >= 0 (the layer always normalises)");
-  if (pos0 < 0 || pos0 > (1LL << 52) - (long long)L) return retention_fail_(RET_ERR_INVALID_ARG, "pos0 out of range");
-  if (!mfma_supported(dk, dv))
-    return retention_fail_(RET_ERR_UNSUPPORTED, "(dk, dv) has no MFMA kernel");
-  if (d_model % 128 || (H * dk) % 128 || (H * dv) % 128)
-    return retention_fail_(RET_ERR_UNSUPPORTED, "d_model, H*dk and H*dv must be multiples of 128");
-  if (L == 0) return retention_fail_(RET_OK, "");
-  if (!x || !w_q || !w_k || !w_v || !w_g || !w_o || !y) return retention_fail_(RET_ERR_INVALID_ARG, "NULL pointer");
-  const void *ptrs[] = {x, w_q, w_k, w_v, w_g, w_o, y, workspace};
-  for (const void *p : ptrs)
-    if ((uintptr_t)p & 15u) return retention_fail_(RET_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-  const MsrLayout m = msr_layout(B, L, H, dk, dv, chunk);
-  if (!workspace || workspace_bytes < m.total) return retention_fail_(RET_ERR_WORKSPACE, "workspace too small");
+// The layer on validated arguments: y = MSR(x) (+ residual, same layout as y).
+static ret_status_t msr_forward(const void *x, const void *w_q, const void *w_k, const void *w_v, const void *w_g,
+                         const void *w_o, void *y, const uint16_t *residual, int B, int L, int d_model, int H, int dk,
+                         int dv, int chunk, const float *gamma, const float *theta, long long pos0, float gn_eps,
+                         char *ws, const MsrLayout &m, hipStream_t st) {
   const size_t T = (size_t)B * L;
-  {
-    const uintptr_t y0 = (uintptr_t)y, y1 = y0 + T * d_model * 2;
-    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + m.total, x0 = (uintptr_t)x, x1 = x0 + T * d_model * 2;
-    if ((y0 < w1 && w0 < y1) || (y0 < x1 && x0 < y1))
-      return retention_fail_(RET_ERR_INVALID_ARG, "y overlaps x or the workspace");
-  }
-  hipStream_t st = (hipStream_t)hip_stream;
-  char *ws = (char *)workspace;
   uint16_t *proj = (uint16_t *)(ws + m.proj), *z = (uint16_t *)(ws + m.z);
   const long long NP = 2LL * H * dk + 2LL * H * dv;  // row length of P
   const long long cq = 0, ck = (long long)H * dk, cv = 2LL * H * dk, cg = cv + (long long)H * dv;
@@ -189,9 +152,58 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
   if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
 
   // 3. output projection
-  e = plain_gemm(z, (const uint16_t *)w_o, (uint16_t *)y, (int)T, d_model, H * dv, d_model, ws + m.blas, st);
+  e = plain_gemm(z, (const uint16_t *)w_o, (uint16_t *)y, (int)T, d_model, H * dv, d_model, ws + m.blas, st, residual);
   if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
   return retention_fail_(RET_OK, "");
+}
+
+
+extern "C" {
+
+size_t msr_layer_fwd_workspace_bytes(int B, int L, int d_model, int H, int dk, int dv, int chunk) {
+  if (B <= 0 || L <= 0 || d_model <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+  if (!mfma_supported(dk, dv)) return 0;
+  return msr_layout(B, L, H, dk, dv, chunk).total;
+}
+
+ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, const void *w_v, const void *w_g,
+                           const void *w_o, void *y, int B, int L, int d_model, int H, int dk, int dv, int chunk,
+                           const float *gamma, const float *theta, long long pos0, float gn_eps, void *workspace,
+                           size_t workspace_bytes, void *hip_stream) {
+  if (B <= 0 || H <= 0 || L < 0 || d_model <= 0 || dk <= 0 || dv <= 0 || chunk <= 0)
+    return retention_fail_(RET_ERR_INVALID_ARG, "sizes must be positive");
+  if (!gamma) return retention_fail_(RET_ERR_INVALID_ARG, "gamma is NULL");
+  if (H > RETENTION_MAX_HEADS) return retention_fail_(RET_ERR_UNSUPPORTED, "too many heads");
+  for (int h = 0; h < H; ++h)
+    if (!(gamma[h] >= 0.0f && gamma[h] <= 1.0f)) return retention_fail_(RET_ERR_INVALID_ARG, "gamma outside [0,1]");
+  if (theta) {
+    if (dk % 2) return retention_fail_(RET_ERR_INVALID_ARG, "rotation needs an even dk");
+    for (int i = 0; i < dk / 2; ++i)
+      if (!std::isfinite(theta[i])) return retention_fail_(RET_ERR_INVALID_ARG, "theta not finite");
+  }
+  if (!(gn_eps >= 0.0f) || !std::isfinite(gn_eps))
+    return retention_fail_(RET_ERR_INVALID_ARG, "gn_eps must be finite and >= 0 (the layer always normalises)");
+  if (pos0 < 0 || pos0 > (1LL << 52) - (long long)L) return retention_fail_(RET_ERR_INVALID_ARG, "pos0 out of range");
+  if (!mfma_supported(dk, dv))
+    return retention_fail_(RET_ERR_UNSUPPORTED, "(dk, dv) has no MFMA kernel");
+  if (d_model % 128 || (H * dk) % 128 || (H * dv) % 128)
+    return retention_fail_(RET_ERR_UNSUPPORTED, "d_model, H*dk and H*dv must be multiples of 128");
+  if (L == 0) return retention_fail_(RET_OK, "");
+  if (!x || !w_q || !w_k || !w_v || !w_g || !w_o || !y) return retention_fail_(RET_ERR_INVALID_ARG, "NULL pointer");
+  const void *ptrs[] = {x, w_q, w_k, w_v, w_g, w_o, y, workspace};
+  for (const void *p : ptrs)
+    if ((uintptr_t)p & 15u) return retention_fail_(RET_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const MsrLayout m = msr_layout(B, L, H, dk, dv, chunk);
+  if (!workspace || workspace_bytes < m.total) return retention_fail_(RET_ERR_WORKSPACE, "workspace too small");
+  const size_t T = (size_t)B * L;
+  {
+    const uintptr_t y0 = (uintptr_t)y, y1 = y0 + T * d_model * 2;
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + m.total, x0 = (uintptr_t)x, x1 = x0 + T * d_model * 2;
+    if ((y0 < w1 && w0 < y1) || (y0 < x1 && x0 < y1))
+      return retention_fail_(RET_ERR_INVALID_ARG, "y overlaps x or the workspace");
+  }
+  return msr_forward(x, w_q, w_k, w_v, w_g, w_o, y, nullptr, B, L, d_model, H, dk, dv, chunk, gamma, theta, pos0,
+                     gn_eps, (char *)workspace, m, (hipStream_t)hip_stream);
 }
 
 size_t msr_layer_step_workspace_bytes(int B, int d_model, int H, int dk, int dv) {
@@ -298,6 +310,74 @@ ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, con
     e = launch_advance_pos(pos, B, st);
     if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
   }
+  return retention_fail_(RET_OK, "");
+}
+
+size_t retnet_block_fwd_workspace_bytes(int B, int L, int d_model, int H, int dk, int dv, int d_ffn, int chunk) {
+  if (B <= 0 || L <= 0 || d_model <= 0 || H <= 0 || dk <= 0 || dv <= 0 || d_ffn <= 0 || chunk <= 0) return 0;
+  if (!mfma_supported(dk, dv)) return 0;
+  const size_t T = (size_t)B * L;
+  return 2 * align256(T * d_model * 2) + align256(T * d_ffn * 2) + msr_layout(B, L, H, dk, dv, chunk).total;
+}
+
+// The pre-LN residual block around the gated layer:
+//   Y = MSR(LN(X)) + X,   out = gelu(LN(Y) W_1^T) W_2^T + Y
+// (LayerNorm without affine; both residual adds run inside the output GEMMs).
+ret_status_t retnet_block_fwd(const void *x, const void *w_q, const void *w_k, const void *w_v, const void *w_g,
+                              const void *w_o, const void *w_1, const void *w_2, void *out, int B, int L, int d_model,
+                              int H, int dk, int dv, int d_ffn, int chunk, const float *gamma, const float *theta,
+                              long long pos0, float gn_eps, float ln_eps, void *workspace, size_t workspace_bytes,
+                              void *hip_stream) {
+  if (B <= 0 || H <= 0 || L < 0 || d_model <= 0 || dk <= 0 || dv <= 0 || d_ffn <= 0 || chunk <= 0)
+    return retention_fail_(RET_ERR_INVALID_ARG, "sizes must be positive");
+  if (!gamma) return retention_fail_(RET_ERR_INVALID_ARG, "gamma is NULL");
+  if (H > RETENTION_MAX_HEADS) return retention_fail_(RET_ERR_UNSUPPORTED, "too many heads");
+  for (int h = 0; h < H; ++h)
+    if (!(gamma[h] >= 0.0f && gamma[h] <= 1.0f)) return retention_fail_(RET_ERR_INVALID_ARG, "gamma outside [0,1]");
+  if (theta) {
+    if (dk % 2) return retention_fail_(RET_ERR_INVALID_ARG, "rotation needs an even dk");
+    for (int i = 0; i < dk / 2; ++i)
+      if (!std::isfinite(theta[i])) return retention_fail_(RET_ERR_INVALID_ARG, "theta not finite");
+  }
+  if (!(gn_eps >= 0.0f) || !std::isfinite(gn_eps) || !(ln_eps >= 0.0f) || !std::isfinite(ln_eps))
+    return retention_fail_(RET_ERR_INVALID_ARG, "gn_eps and ln_eps must be finite and >= 0");
+  if (pos0 < 0 || pos0 > (1LL << 52) - (long long)L) return retention_fail_(RET_ERR_INVALID_ARG, "pos0 out of range");
+  if (!mfma_supported(dk, dv)) return retention_fail_(RET_ERR_UNSUPPORTED, "(dk, dv) has no MFMA kernel");
+  if (d_model % 128 || (H * dk) % 128 || (H * dv) % 128 || d_ffn % 128 || d_model > 8192)
+    return retention_fail_(RET_ERR_UNSUPPORTED,
+                           "d_model, H*dk, H*dv and d_ffn must be multiples of 128, and d_model <= 8192");
+  if (L == 0) return retention_fail_(RET_OK, "");
+  if (!x || !w_q || !w_k || !w_v || !w_g || !w_o || !w_1 || !w_2 || !out)
+    return retention_fail_(RET_ERR_INVALID_ARG, "NULL pointer");
+  const void *ptrs[] = {x, w_q, w_k, w_v, w_g, w_o, w_1, w_2, out, workspace};
+  for (const void *p : ptrs)
+    if ((uintptr_t)p & 15u) return retention_fail_(RET_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t need = retnet_block_fwd_workspace_bytes(B, L, d_model, H, dk, dv, d_ffn, chunk);
+  if (!workspace || workspace_bytes < need) return retention_fail_(RET_ERR_WORKSPACE, "workspace too small");
+  const size_t T = (size_t)B * L;
+  {
+    const uintptr_t o0 = (uintptr_t)out, o1 = o0 + T * d_model * 2;
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need, x0 = (uintptr_t)x, x1 = x0 + T * d_model * 2;
+    if ((o0 < w1 && w0 < o1) || (o0 < x1 && x0 < o1))
+      return retention_fail_(RET_ERR_INVALID_ARG, "out overlaps x or the workspace");
+  }
+  hipStream_t st = (hipStream_t)hip_stream;
+  char *ws = (char *)workspace;
+  uint16_t *h = (uint16_t *)ws, *yb = (uint16_t *)(ws + align256(T * d_model * 2));
+  uint16_t *u = (uint16_t *)(ws + 2 * align256(T * d_model * 2));
+  char *mws = ws + 2 * align256(T * d_model * 2) + align256(T * d_ffn * 2);
+  hipError_t e = launch_layernorm_bf16((const uint16_t *)x, h, (long long)T, d_model, ln_eps, st);
+  if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  ret_status_t s = msr_forward(h, w_q, w_k, w_v, w_g, w_o, yb, (const uint16_t *)x, B, L, d_model, H, dk, dv, chunk,
+                               gamma, theta, pos0, gn_eps, mws, msr_layout(B, L, H, dk, dv, chunk), st);
+  if (s != RET_OK) return s;
+  void *blas = mws + msr_layout(B, L, H, dk, dv, chunk).blas;
+  if ((e = launch_layernorm_bf16(yb, h, (long long)T, d_model, ln_eps, st)) != hipSuccess ||
+      (e = plain_gemm(h, (const uint16_t *)w_1, u, (int)T, d_ffn, d_model, d_ffn, blas, st)) != hipSuccess ||
+      (e = launch_gelu_bf16(u, (long long)T * d_ffn, st)) != hipSuccess ||
+      (e = plain_gemm(u, (const uint16_t *)w_2, (uint16_t *)out, (int)T, d_model, d_ffn, d_model, blas, st, yb)) !=
+          hipSuccess)
+    return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
   return retention_fail_(RET_OK, "");
 }
 

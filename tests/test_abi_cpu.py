@@ -23,7 +23,7 @@ FAKE4 = ctypes.c_void_p(0x400000)
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(retention_\w+|msr_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(retention_\w+|msr_\w+|retnet_\w+)\s*\(", src)))
 
 
 def _f(vals):
@@ -168,3 +168,19 @@ def test_backward_rejects_and_workspace():
     assert call(gamma=_f([0.9, -0.1])) == INVALID
     assert call(wsb=need - 1) == WORKSPACE
     assert call(dq=FAKE) == INVALID  # a gradient overlapping an input
+
+
+def test_block_rejects():
+    L = rn.lib()
+    g = _f([0.9] * 2)
+    INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+    need = L.retnet_block_fwd_workspace_bytes(1, 64, 256, 2, 64, 128, 512, 64)
+    assert need > L.msr_layer_fwd_workspace_bytes(1, 64, 256, 2, 64, 128, 64)
+
+    def call(d_ffn=512, ln_eps=1e-5, wsb=need, w_1=FAKE3):
+        return L.retnet_block_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, w_1, FAKE3, FAKE2, 1, 64, 256, 2, 64, 128,
+                                  d_ffn, 64, g, None, 0, 1e-5, ln_eps, FAKE4, wsb, None)
+    assert call(d_ffn=500) == UNSUPPORTED
+    assert call(ln_eps=-1.0) == INVALID
+    assert call(w_1=None) == INVALID
+    assert call(wsb=need - 1) == WORKSPACE

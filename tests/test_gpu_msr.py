@@ -185,3 +185,46 @@ def test_msr_fused_weights_match_separate():
                          for t in range(8)], 1)
     torch.cuda.synchronize()
     _tol.assert_bf16(steps, ref[:, :8], slice_dims=0, what="fused weights, steps")
+
+
+def _block_weights(dm, H, dk, dv, dff, seed, w_std=0.05):
+    bf = torch.bfloat16
+    return _step_weights(dm, H, dk, dv, seed, w_std) + [randn((dff, dm), seed + 8, w_std, bf),
+                                                         randn((dm, dff), seed + 9, w_std, bf)]
+
+
+@pytest.mark.parametrize("B,L,dm,H,dk,dv,dff,chunk", [(2, 130, 256, 2, 64, 128, 512, 64),
+                                                      (1, 200, 512, 2, 256, 512, 1024, 128)])
+def test_retnet_block_small(B, L, dm, H, dk, dv, dff, chunk):
+    """The pre-LN residual block (LayerNorm, gated layer, residual, LayerNorm, gelu
+    FFN, residual) against the oracle."""
+    x = randn((B, L, dm), 1300 + dk, 1.0, torch.bfloat16)
+    w = _block_weights(dm, H, dk, dv, dff, 1300 + dk)
+    g, th = multiscale_gamma(H), rotation_theta(dk)
+    y = rn.retnet_block_fwd(x.to(DEV), *[t.to(DEV) for t in w], H, dk, dv, chunk, g, th, pos0=2)
+    torch.cuda.synchronize()
+    ref = oracle.retnet_block(x, *w, H, dk, dv, g, th, pos0=2)
+    _tol.assert_bf16(y, ref, slice_dims=0, what="block")
+    _tol.assert_bf16(y, ref, slice_dims=1, what="block per batch")
+
+
+def test_retnet_block_full_size_sampled():
+    """The layer workload's dimensions with an FFN of width 2 d_model (4096): sampled
+    rows against the oracle (causal, so only the prefix up to each row is used)."""
+    wl = MSRWorkload()
+    x, wq, wk, wv, wg, wo = wl.inputs()
+    dff = 2 * wl.d_model
+    w1 = randn((dff, wl.d_model), 5008, wl.w_std, torch.bfloat16)
+    w2 = randn((wl.d_model, dff), 5009, wl.w_std, torch.bfloat16)
+    g, th = wl.gamma(), wl.theta()
+    dev = [t.to(DEV) for t in (x, wq, wk, wv, wg, wo, w1, w2)]
+    y = rn.retnet_block_fwd(*dev, wl.H, wl.dk, wl.dv, wl.chunk, g, th, gn_eps=wl.gn_eps)
+    torch.cuda.synchronize()
+    yc = y.float().cpu().numpy()
+    samples = {0: [0, 1, 700], 2: [5, 512]}
+    for b, ls in samples.items():
+        lmax = max(ls) + 1
+        ref = oracle.retnet_block(x[b:b + 1, :lmax], wq, wk, wv, wg, wo, w1, w2, wl.H, wl.dk, wl.dv, g, th,
+                                  gn_eps=wl.gn_eps, tokens=[(0, l) for l in ls])
+        got = np.stack([yc[b, l] for l in ls])
+        _tol.assert_bf16(got, ref, slice_dims=0, what=f"block full-size batch {b}")
