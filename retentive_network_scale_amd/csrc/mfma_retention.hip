@@ -884,7 +884,30 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           }
         }
       }
-      epilogue_store<RB, RW, DV, PAIR>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
+      if (PAIR && !a.use_gn && !a.gate && a.out_bf16 && !a.out_rot && !a.out_rev) {
+        // Plain bf16 output: stage the block through the V tile's LDS (free until
+        // the next visit's commit) so that every store writes whole rows.
+        constexpr int DVP = DV + 8;  // 16-byte aligned rows
+        static_assert(BT * DVP <= DV * LDT, "output staging fits in Vt");
+        uint16_t *const Os = Vt;
+        __syncthreads();  // every wave has finished reading Vt
+#pragma unroll
+        for (int qb4 = 0; qb4 < 4; ++qb4)
+          *(u32x4 *)(Os + (16 * qb4 + l16) * DVP + w * RW + 8 * g) =
+              u32x4{pack_bf2(ot[0][qb4][0], ot[0][qb4][1]), pack_bf2(ot[0][qb4][2], ot[0][qb4][3]),
+                    pack_bf2(ot[RB - 1][qb4][0], ot[RB - 1][qb4][1]), pack_bf2(ot[RB - 1][qb4][2], ot[RB - 1][qb4][3])};
+        __syncthreads();
+        const int nvalid = min(BT, c0 + Cc - q0);
+#pragma unroll
+        for (int i = 0; i < BT * (DV / 8) / NT; ++i) {
+          const int c = tid + NT * i, row = c / (DV / 8), c8 = c % (DV / 8);
+          if (row < nvalid)
+            __builtin_nontemporal_store(*(const u32x4 *)(Os + row * DVP + 8 * c8),
+                                        (u32x4 *)((uint16_t *)a.o + obase + (long long)(q0 + row) * a.o_sn + 8 * c8));
+        }
+      } else {
+        epilogue_store<RB, RW, DV, PAIR>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
+      }
     }
   }
 }
