@@ -375,11 +375,12 @@ __device__ __forceinline__ void unrotate_pairs(const RetArgs &a, float *x, long 
   }
 }
 
-template <int RB, int RW, int DV, bool PAIR = false>
-__device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB][4], float (*red)[BT], int b, int h,
-                                               int q0, int nvalid, long long obase, int w, int g, int l16) {
-  static_assert(!PAIR || RB == 2, "paired column order needs two row blocks");
-  if (a.use_gn) {
+// Per-(query, head) GroupNorm over the DV columns held by the 8 waves (rows of
+// O^T in the accumulators), in place.  Contains barriers: call from all threads.
+template <int RB, int DV>
+__device__ __forceinline__ void epilogue_groupnorm(const RetArgs &a, f32x4 (&ot)[RB][4], float (*red)[BT], int w,
+                                                   int g, int l16) {
+  {
     float mean[4], inv[4];
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
@@ -420,6 +421,70 @@ __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB]
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = (ot[rb][qb4] - mean[qb4]) * inv[qb4];
   }
+}
+
+// Output of a 64-query block (bf16): the accumulators (after GroupNorm) go to
+// LDS as rows of O in the Os buffer (pitch DV + 8), then every store writes whole
+// 16-byte pieces of rows, coalesced across lanes; the gate, the inverse rotation
+// and the row reversal are applied in that row-wise pass.  Os must be free
+// (its readers done) on entry: the first barrier orders that.
+template <int RB, int RW, int DV, bool PAIR>
+__device__ __forceinline__ void epilogue_staged(const RetArgs &a, f32x4 (&ot)[RB][4], uint16_t *Os, int b, int h,
+                                                int q0, int nvalid, long long obase, int w, int g, int l16) {
+  constexpr int DVP = DV + 8;
+  __syncthreads();
+#pragma unroll
+  for (int qb4 = 0; qb4 < 4; ++qb4) {
+    const int row = 16 * qb4 + l16;
+    if constexpr (PAIR) {
+      *(u32x4 *)(Os + row * DVP + w * RW + 8 * g) =
+          u32x4{pack_bf2(ot[0][qb4][0], ot[0][qb4][1]), pack_bf2(ot[0][qb4][2], ot[0][qb4][3]),
+                pack_bf2(ot[1][qb4][0], ot[1][qb4][1]), pack_bf2(ot[1][qb4][2], ot[1][qb4][3])};
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        *(u32x2 *)(Os + row * DVP + w * RW + 16 * rb + 4 * g) =
+            pack4(ot[rb][qb4][0], ot[rb][qb4][1], ot[rb][qb4][2], ot[rb][qb4][3]);
+    }
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < BT * (DV / 8) / NT; ++i) {
+    const int c = tid + NT * i, row = c / (DV / 8), col = 8 * (c % (DV / 8));
+    if (row >= nvalid) continue;
+    u32x4 o = *(const u32x4 *)(Os + row * DVP + col);
+    if (a.gate || a.out_rot) {
+      const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(ow[e] << 16);
+        x[2 * e + 1] = __uint_as_float(ow[e] & 0xffff0000u);
+      }
+      if (a.gate) {
+        const long long go = (long long)b * a.g_sb + (long long)h * a.g_sh + (long long)(q0 + row) * a.g_sn + col;
+        const u32x4 gg = *(const u32x4 *)(a.gate + go);
+        const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] *= gate_value(__uint_as_float(gw[e] << 16), a.gate_swish);
+          x[2 * e + 1] *= gate_value(__uint_as_float(gw[e] & 0xffff0000u), a.gate_swish);
+        }
+      }
+      if (a.out_rot) unrotate_pairs<8>(a, x, a.pos0 + (a.out_rev ? a.L - 1 - (q0 + row) : q0 + row), col / 2);
+      o = u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
+    }
+    const int n = a.out_rev ? a.L - 1 - (q0 + row) : q0 + row;
+    __builtin_nontemporal_store(o, (u32x4 *)((uint16_t *)a.o + obase + (long long)n * a.o_sn + col));
+  }
+}
+
+template <int RB, int RW, int DV, bool PAIR = false>
+__device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB][4], float (*red)[BT], int b, int h,
+                                               int q0, int nvalid, long long obase, int w, int g, int l16) {
+  static_assert(!PAIR || RB == 2, "paired column order needs two row blocks");
+  if (a.use_gn) epilogue_groupnorm<RB, DV>(a, ot, red, w, g, l16);
   if constexpr (PAIR) {
 #pragma unroll
     for (int qb4 = 0; qb4 < 4; ++qb4) {
@@ -660,7 +725,13 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
       }
     }
   }
-  epilogue_store<RB, RW, DV>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
+  if (a.out_bf16) {  // staged through the V tile's LDS, free after the last visit
+    static_assert(BT * (DV + 8) <= DV * LDT, "output staging fits in Vt");
+    if (a.use_gn) epilogue_groupnorm<RB, DV>(a, ot, red, w, g, l16);
+    epilogue_staged<RB, RW, DV, false>(a, ot, Vt, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
+  } else {
+    epilogue_store<RB, RW, DV>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
+  }
 }
 
 // ---------------------------------------------------------------- segment output kernel
@@ -884,27 +955,11 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           }
         }
       }
-      if (PAIR && !a.use_gn && !a.gate && a.out_bf16 && !a.out_rot && !a.out_rev) {
-        // Plain bf16 output: stage the block through the V tile's LDS (free until
-        // the next visit's commit) so that every store writes whole rows.
-        constexpr int DVP = DV + 8;  // 16-byte aligned rows
-        static_assert(BT * DVP <= DV * LDT, "output staging fits in Vt");
-        uint16_t *const Os = Vt;
-        __syncthreads();  // every wave has finished reading Vt
-#pragma unroll
-        for (int qb4 = 0; qb4 < 4; ++qb4)
-          *(u32x4 *)(Os + (16 * qb4 + l16) * DVP + w * RW + 8 * g) =
-              u32x4{pack_bf2(ot[0][qb4][0], ot[0][qb4][1]), pack_bf2(ot[0][qb4][2], ot[0][qb4][3]),
-                    pack_bf2(ot[RB - 1][qb4][0], ot[RB - 1][qb4][1]), pack_bf2(ot[RB - 1][qb4][2], ot[RB - 1][qb4][3])};
-        __syncthreads();
-        const int nvalid = min(BT, c0 + Cc - q0);
-#pragma unroll
-        for (int i = 0; i < BT * (DV / 8) / NT; ++i) {
-          const int c = tid + NT * i, row = c / (DV / 8), c8 = c % (DV / 8);
-          if (row < nvalid)
-            __builtin_nontemporal_store(*(const u32x4 *)(Os + row * DVP + 8 * c8),
-                                        (u32x4 *)((uint16_t *)a.o + obase + (long long)(q0 + row) * a.o_sn + 8 * c8));
-        }
+      if (a.out_bf16) {
+        // bf16 output staged through the V tile's LDS, free until the next visit's commit
+        static_assert(BT * (DV + 8) <= DV * LDT, "output staging fits in Vt");
+        if (a.use_gn) epilogue_groupnorm<RB, DV>(a, ot, red, w, g, l16);
+        epilogue_staged<RB, RW, DV, PAIR>(a, ot, Vt, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
       } else {
         epilogue_store<RB, RW, DV, PAIR>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
       }
