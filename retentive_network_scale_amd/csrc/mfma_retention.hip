@@ -70,6 +70,24 @@ __device__ __forceinline__ u32x4 ld_op(const uint16_t *row, int k0, int g) {
   return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
+// The same operand from a row-major tile T[k][m] (rows = the K index, pitch ldr
+// elements): lane group g needs T[k0+4g+j][m0+l16] and T[k0+16+4g+j][m0+l16],
+// j < 4.  ds_read_b64_tr_b16 returns to lane r of a 16-lane group element j of
+// the 8-byte piece addressed by lane 4j + r/4; so lane p points at row
+// k0 + 4g + p/4, columns m0 + 4(p%4) .. +3 (8-byte aligned).  Conflict-free
+// when the pitch in dwords is 8 mod 32.
+typedef short tr_v4s __attribute__((ext_vector_type(4)));
+// Row pitch (elements) of a row-major tile of D columns for ld_op_tr: the
+// smallest length >= D whose dword count is 8 mod 32.
+__host__ __device__ constexpr int tr_pitch(int D) { return 2 * (((D / 2 - 8 + 31) / 32) * 32 + 8); }
+__device__ __forceinline__ u32x4 ld_op_tr(const uint16_t *T, int ldr, int k0, int m0, int g, int l16) {
+  const uint16_t *p0 = T + (k0 + 4 * g + (l16 >> 2)) * ldr + m0 + 4 * (l16 & 3);
+  const tr_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr_v4s *)p0);
+  const tr_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr_v4s *)(p0 + 16 * ldr));
+  const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l.x, l.y, h.x, h.y};
+}
+
 __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
   return u32x2{pack_bf2(a, b), pack_bf2(c, d)};
 }
@@ -203,12 +221,13 @@ struct TileIO {
   }
 
   // rows:  dst[t * ldr + col]            (token-major, bf16; lo part to dstLo when LO)
-  // trans: dstT[col * LDT + t] * zeta_t  (token-minor), zeta_t = gamma^(zoff - t) when `zeta`
+  // trans: dstT[col * LDT + t] * zeta_t  (token-minor), zeta_t = gamma^(zoff - t) when `zeta`;
+  //        with ZR instead dstT[t * ldz + col] * zeta_t (token-major, 16-byte stores, ldz % 8 == 0)
   // Rotation (rot): token t of the tile sits at absolute position p0 + t.
-  template <bool ROWS, bool TRANS, bool LO>
+  template <bool ROWS, bool TRANS, bool LO, bool ZR = false>
   __device__ __forceinline__ void commit(bool rot, long long p0, const float *theta_s, const float *rev_s,
                                          uint16_t *dst, int ldr, uint16_t *dstLo, uint16_t *dstT, bool zeta,
-                                         float zlg, int zoff) const {
+                                         float zlg, int zoff, int ldz = 0) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int idx = threadIdx.x + NT * i;
@@ -274,6 +293,14 @@ struct TileIO {
           const int d = zoff - (TPT * tg + r);  // d < 0: a zero-filled token past the chunk
           z[r] = zeta ? (d >= 0 ? dpow(zlg, d) : 0.0f) : 1.0f;
         }
+        if constexpr (ZR) {
+#pragma unroll
+          for (int r = 0; r < TPT; ++r)
+            *(u32x4 *)(dstT + (TPT * tg + r) * ldz + 8 * c8) =
+                u32x4{pack_bf2(x[r][0] * z[r], x[r][1] * z[r]), pack_bf2(x[r][2] * z[r], x[r][3] * z[r]),
+                      pack_bf2(x[r][4] * z[r], x[r][5] * z[r]), pack_bf2(x[r][6] * z[r], x[r][7] * z[r])};
+          continue;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           uint16_t *row = dstT + (8 * c8 + e) * LDT + TPT * tg;
@@ -324,6 +351,70 @@ struct TileIO {
           *(u32x2 *)(row + 4) = u32x2{pk[2], pk[3]};
         }
       }
+    }
+  }
+};
+
+// Row-major staging of a 64-token tile of a [tokens][D] bf16 tensor: work item =
+// (token t, 16-byte column chunk c8) with c8 fastest across lanes, so a wave
+// reads whole rows from memory and writes whole rows to LDS (16-byte stores, no
+// bank conflicts).  MFMA operands are then read with ld_op (along the row) or
+// ld_op_tr (across rows).
+template <int D>
+struct RowIO {
+  static constexpr int C8 = D / 8;
+  static constexpr int ITEMS = BT * C8;
+  static constexpr int NI = ITEMS / NT;
+  static_assert(ITEMS % NT == 0, "whole items per thread");
+  uint4 raw[NI];
+
+  __device__ __forceinline__ void fetch(const uint16_t *src, long long stride, int valid) {
+    const int nbytes = valid > 0 ? (int)((long long)valid * stride * 2) : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nbytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = threadIdx.x + NT * i, t = idx / C8, c8 = idx % C8;
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, (t * (int)stride + 8 * c8) * 2, 0, 0);
+      raw[i] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+  }
+
+  // dst[t * ldr + col] = raw, optionally rotated (token t at position p0 + t) and
+  // scaled by zeta_t = gamma^(zoff - t) (0 for t > zoff: a zero-filled row).
+  template <bool ROT, bool ZETA>
+  __device__ __forceinline__ void commit(uint16_t *dst, int ldr, long long p0, const float *theta_s, float zlg,
+                                         int zoff) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = threadIdx.x + NT * i, t = idx / C8, c8 = idx % C8;
+      uint4 o = raw[i];
+      if (ROT || ZETA) {
+        const uint32_t wv[4] = {o.x, o.y, o.z, o.w};
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = __uint_as_float(wv[e] << 16);
+          x[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+        }
+        if constexpr (ROT) {
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const float rv = base_rev(p0 + t, theta_s[4 * c8 + pp]);
+            const float sn = __builtin_amdgcn_sinf(rv), c = __builtin_amdgcn_cosf(rv);
+            const float re = x[2 * pp], im = x[2 * pp + 1];
+            x[2 * pp] = re * c - im * sn;
+            x[2 * pp + 1] = re * sn + im * c;
+          }
+        }
+        if constexpr (ZETA) {
+          const int d = zoff - t;
+          const float z = d >= 0 ? dpow(zlg, d) : 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] *= z;
+        }
+        o = make_uint4(pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7]));
+      }
+      *(uint4 *)(dst + t * ldr + 8 * c8) = o;
     }
   }
 };
@@ -754,18 +845,21 @@ template <int DK, int DV, bool SPLIT, bool RES>
 __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, const float *seg_state) {
   using T = Tile<DK, DV>;
   constexpr int LDQ = T::LDQ, RW = T::RW, RB = T::RB, KS = T::KS, DKB = T::DKB;
-  constexpr bool PAIR = RB == 2;
+  constexpr bool PAIR = false;
+  // V tiles and the zeta-scaled keys of the update are kept token-major and read
+  // across rows (ld_op_tr)
+  constexpr int LDV = tr_pitch(DV), LDZ = tr_pitch(DK);
   static_assert(!(RES && SPLIT), "resident keys carry no lo part");
-  // Qs (rotated query block, bf16) is read only before the key loop and Kt
-  // (zeta-scaled transposed keys of the update) only inside it: shared storage.
-  constexpr int QK_SZ = BT * LDQ > DK * LDT ? BT * LDQ : DK * LDT;
+  // Qs (rotated query block, bf16) is read only before the key loop and Kz
+  // (zeta-scaled keys of the update) only inside it: shared storage.
+  constexpr int QK_SZ = BT * LDQ > BT * LDZ ? BT * LDQ : BT * LDZ;
   __shared__ __attribute__((aligned(16))) uint16_t QKs[QK_SZ];
   __shared__ __attribute__((aligned(16))) uint16_t Ks[(RES ? KRES : 1) * BT * LDQ];
   __shared__ __attribute__((aligned(16))) uint16_t KsL[SPLIT ? BT * LDQ : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t Vr[BT * LDV];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[BT * LDT];
   uint16_t *const Qs = QKs;
-  uint16_t *const Kt = QKs;
+  uint16_t *const Kz = QKs;
   __shared__ float theta_s[DK / 2], rev_s[DK / 2];
   __shared__ float red[8][BT];
   __shared__ float dt[DT_SZ];
@@ -805,7 +899,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           st[dkb][rb][i] = S_in[(long long)(16 * dkb + 4 * g + i) * DV + w * RW + dv_of<PAIR>(rb, l16)];
   }
   TileIO<DK> qio, kio;
-  TileIO<DV> vio;
+  RowIO<DV> vio;
   {
     const int Cc = min(a.chunk, a.L - t_lo);
     qio.fetch(q + (long long)t_lo * a.q_sn, a.q_sn, min(BT, Cc));
@@ -873,18 +967,18 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
         __syncthreads();
         if (!RES || kb == qb) {
           if (upd)
-            kio.template commit<true, true, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Kb, LDQ, KsL, Kt, true, lg,
-                                                   Cc - 1 - (k0 - c0));
+            kio.template commit<true, true, SPLIT, true>(rot, a.pos0 + k0, theta_s, rev_s, Kb, LDQ, KsL, Kz, true,
+                                                         lg, Cc - 1 - (k0 - c0), LDZ);
           else
             kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Kb, LDQ, KsL, nullptr, false,
                                                     0.f, 0);
-        } else if (upd) {  // resident block: zeta-scaled transposed copy from LDS
+        } else if (upd) {  // resident block: zeta-scaled copy from LDS
           TileIO<DK> kres;
           kres.load_lds(Kb, LDQ);
-          kres.template commit<false, true, false>(false, 0, theta_s, rev_s, nullptr, LDQ, nullptr, Kt, true, lg,
-                                                   Cc - 1 - (k0 - c0));
+          kres.template commit<false, true, false, true>(false, 0, theta_s, rev_s, nullptr, LDQ, nullptr, Kz, true,
+                                                         lg, Cc - 1 - (k0 - c0), LDZ);
         }
-        vio.commit_trans(Vt);
+        vio.template commit<false, false>(Vr, LDV, 0, theta_s, 0.0f, 0);
         __syncthreads();
         // next visit: next key block of this query block, else the first key block
         // of the next query block (of this chunk, or of the next chunk).  Its loads
@@ -937,7 +1031,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
         for (int ks = 0; ks < 2; ++ks) {
           u32x4 av[RB];
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) av[rb] = ld_op(Vt + (w * RW + dv_of<PAIR>(rb, l16)) * LDT, 32 * ks, g);
+          for (int rb = 0; rb < RB; ++rb) av[rb] = ld_op_tr(Vr, LDV, 32 * ks, w * RW + 16 * rb, g, l16);
 #pragma unroll
           for (int qb4 = 0; qb4 < 4; ++qb4) {
             const u32x4 bp = ld_op(Ps + (16 * qb4 + l16) * LDT, 32 * ks, g);
@@ -948,7 +1042,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
             // S += (zeta K)^T V over this key block
 #pragma unroll
             for (int dkb = 0; dkb < DKB; ++dkb) {
-              const u32x4 ak = ld_op(Kt + (16 * dkb + l16) * LDT, 32 * ks, g);
+              const u32x4 ak = ld_op_tr(Kz, LDZ, 32 * ks, 16 * dkb, g, l16);
 #pragma unroll
               for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = mfma(ak, av[rb], st[dkb][rb]);
             }
@@ -957,9 +1051,9 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
       }
       if (a.out_bf16) {
         // bf16 output staged through the V tile's LDS, free until the next visit's commit
-        static_assert(BT * (DV + 8) <= DV * LDT, "output staging fits in Vt");
+        static_assert(BT * (DV + 8) <= BT * LDV, "output staging fits in Vr");
         if (a.use_gn) epilogue_groupnorm<RB, DV>(a, ot, red, w, g, l16);
-        epilogue_staged<RB, RW, DV, PAIR>(a, ot, Vt, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
+        epilogue_staged<RB, RW, DV, PAIR>(a, ot, Vr, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
       } else {
         epilogue_store<RB, RW, DV, PAIR>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
       }
@@ -994,9 +1088,11 @@ template <int DK, int DVW>
 __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, float *seg_state, uint16_t *locT) {
   using T = Tile<DK, DVW>;
   constexpr int RW = T::RW, RB = T::RB, DKB = T::DKB;
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DVW * LDT];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][DK * LDT];
-  __shared__ float theta_s[DK / 2], rev_s[DK / 2];
+  constexpr int LDK = tr_pitch(DK), LDV = tr_pitch(DVW);
+  // row-major (token-major) tiles, read across rows by ld_op_tr
+  __shared__ __attribute__((aligned(16))) uint16_t Vr[2][BT * LDV];
+  __shared__ __attribute__((aligned(16))) uint16_t Kr[2][BT * LDK];
+  __shared__ float theta_s[DK / 2];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int task = xcd_task(blockIdx.x, geo.ntasks);
   if (task < 0) return;
@@ -1008,10 +1104,7 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
   const uint16_t *k = (const uint16_t *)a.k + (long long)b * a.q_sb + (long long)h * a.q_sh;
   const uint16_t *v = (const uint16_t *)a.v + (long long)b * a.v_sb + (long long)h * a.v_sh + split * DVW;
   if (a.use_theta)
-    for (int i = tid; i < DK / 2; i += NT) {
-      theta_s[i] = a.theta[i];
-      rev_s[i] = (float)((double)a.theta[i] * 0.15915494309189535);
-    }
+    for (int i = tid; i < DK / 2; i += NT) theta_s[i] = a.theta[i];
   __syncthreads();
   const int c_lo = seg * geo.seg_chunks;
   const int c_hi = min(geo.nchunks, c_lo + geo.seg_chunks);
@@ -1021,8 +1114,8 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
   for (int dkb = 0; dkb < DKB; ++dkb)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  TileIO<DK> kio[2];
-  TileIO<DVW> vio[2];
+  RowIO<DK> kio[2];
+  RowIO<DVW> vio[2];
   // pf: the next block to fetch; a block past the segment fetches no rows
   BlockPos cur{t_lo, t_lo, min(a.chunk, a.L - t_lo)}, pf = cur;
 #pragma unroll
@@ -1061,9 +1154,12 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
       }
       // buffer `buf` was last read two blocks ago; the barrier of the previous
       // block ordered those reads before this write
-      kio[s].template commit<false, true, false>(a.use_theta, a.pos0 + cur.k0, theta_s, rev_s, nullptr, 0, nullptr,
-                                                 Kt[buf], true, lg, cur.c0 + cur.Cc - 1 - cur.k0);
-      vio[s].commit_trans(Vt[buf]);
+      const int zoff = cur.c0 + cur.Cc - 1 - cur.k0;
+      if (a.use_theta)
+        kio[s].template commit<true, true>(Kr[buf], LDK, a.pos0 + cur.k0, theta_s, lg, zoff);
+      else
+        kio[s].template commit<false, true>(Kr[buf], LDK, 0, theta_s, lg, zoff);
+      vio[s].template commit<false, false>(Vr[buf], LDV, 0, theta_s, 0.0f, 0);
       __syncthreads();
       {  // this register set now takes the block two ahead
         const int nv = pf.k0 < t_hi ? pf.valid() : 0;
@@ -1075,10 +1171,10 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
       for (int ks = 0; ks < 2; ++ks) {
         u32x4 bv[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) bv[rb] = ld_op(Vt[buf] + (w * RW + 16 * rb + l16) * LDT, 32 * ks, g);
+        for (int rb = 0; rb < RB; ++rb) bv[rb] = ld_op_tr(Vr[buf], LDV, 32 * ks, w * RW + 16 * rb, g, l16);
 #pragma unroll
         for (int dkb = 0; dkb < DKB; ++dkb) {
-          const u32x4 ak = ld_op(Kt[buf] + (16 * dkb + l16) * LDT, 32 * ks, g);
+          const u32x4 ak = ld_op_tr(Kr[buf], LDK, 32 * ks, 16 * dkb, g, l16);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = mfma(ak, bv[rb], st[dkb][rb]);
         }
