@@ -56,7 +56,7 @@ constexpr int BT = 64;    // query / key block (tokens)
 // consecutive rows; a row stride of 34 dwords (mod 32: 2) puts those 16 reads
 // on 32 distinct banks.  Rows are therefore only 8-byte aligned and every LDS
 // access is at most 8 bytes wide.
-constexpr int LDT = BT + 4;  // token-minor tiles (Vt, Kt, Ps): 136 bytes
+constexpr int LDT = BT + 4;  // token-minor tiles (Ps, transposed keys): 136 bytes
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -312,43 +312,6 @@ struct TileIO {
             *(u32x2 *)row = pack4(x[0][e] * z[0], x[1][e] * z[1], x[2][e] * z[2], x[3][e] * z[3]);
             *(u32x2 *)(row + 4) = pack4(x[4][e] * z[4], x[5][e] * z[5], x[6][e] * z[6], x[7][e] * z[7]);
           }
-        }
-      }
-    }
-  }
-
-  // Transposed copy without arithmetic (V tiles): 16-bit halves regrouped with
-  // byte permutes, dstT[col * LDT + t].
-  __device__ __forceinline__ void commit_trans(uint16_t *dstT) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int idx = threadIdx.x + NT * i;
-      if (idx >= ITEMS) continue;
-      int tg, c8;
-      item(idx, tg, c8);
-      uint32_t wv[TPT][4];
-#pragma unroll
-      for (int r = 0; r < TPT; ++r) {
-        wv[r][0] = raw[i][r].x;
-        wv[r][1] = raw[i][r].y;
-        wv[r][2] = raw[i][r].z;
-        wv[r][3] = raw[i][r].w;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // column e of tokens r, r+1: low halves (e even) or high halves (e odd)
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t pk[TPT / 2];
-#pragma unroll
-        for (int r = 0; r < TPT; r += 2) pk[r / 2] = __builtin_amdgcn_perm(wv[r + 1][e >> 1], wv[r][e >> 1], sel);
-        uint16_t *row = dstT + (8 * c8 + e) * LDT + TPT * tg;
-        if constexpr (TPT == 2) {
-          *(uint32_t *)row = pk[0];
-        } else if constexpr (TPT == 4) {
-          *(u32x2 *)row = u32x2{pk[0], pk[1]};
-        } else {
-          *(u32x2 *)row = u32x2{pk[0], pk[1]};
-          *(u32x2 *)(row + 4) = u32x2{pk[2], pk[3]};
         }
       }
     }
@@ -659,10 +622,11 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
                                                     const uint16_t *locT) {
   using T = Tile<DK, DV>;
   constexpr int LDQ = T::LDQ, RW = T::RW, RB = T::RB, KS = T::KS;
+  constexpr int LDV = tr_pitch(DV);  // token-major V tile, read across rows (ld_op_tr)
   // The query block is staged through Ks / KsL (free until the key loop starts).
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BT * LDQ];
   __shared__ __attribute__((aligned(16))) uint16_t KsL[SPLIT ? BT * LDQ : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t Vr[BT * LDV];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[BT * LDT];
   __shared__ float theta_s[DK / 2], rev_s[DK / 2];
   __shared__ float red[8][BT];
@@ -702,7 +666,7 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   fill_decay_table(dt, lg, NT);
 
   TileIO<DK> qio, kio;
-  TileIO<DV> vio;
+  RowIO<DV> vio;
   qio.fetch(q + (long long)q0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - q0));
   kio.fetch(k + (long long)c0 * a.q_sn, a.q_sn, min(BT, Cc));
   vio.fetch(v + (long long)c0 * a.v_sn, a.v_sn, min(BT, Cc));
@@ -774,7 +738,7 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
     const float gdel = delta ? dpow(lg, 64 * (delta - 1)) : 1.0f;
     __syncthreads();
     kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Ks, LDQ, KsL, nullptr, false, 0.f, 0);
-    vio.commit_trans(Vt);
+    vio.template commit<false, false>(Vr, LDV, 0, theta_s, 0.0f, 0);
     __syncthreads();
     if (kb < qb) {
       const int n0 = k0 + BT;
@@ -807,7 +771,7 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 av[RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) av[rb] = ld_op(Vt + (w * RW + 16 * rb + l16) * LDT, 32 * ks, g);
+      for (int rb = 0; rb < RB; ++rb) av[rb] = ld_op_tr(Vr, LDV, 32 * ks, w * RW + 16 * rb, g, l16);
 #pragma unroll
       for (int qb4 = 0; qb4 < 4; ++qb4) {
         const u32x4 bp = ld_op(Ps + (16 * qb4 + l16) * LDT, 32 * ks, g);
@@ -817,9 +781,9 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
     }
   }
   if (a.out_bf16) {  // staged through the V tile's LDS, free after the last visit
-    static_assert(BT * (DV + 8) <= DV * LDT, "output staging fits in Vt");
+    static_assert(BT * (DV + 8) <= BT * LDV, "output staging fits in Vr");
     if (a.use_gn) epilogue_groupnorm<RB, DV>(a, ot, red, w, g, l16);
-    epilogue_staged<RB, RW, DV, false>(a, ot, Vt, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
+    epilogue_staged<RB, RW, DV, false>(a, ot, Vr, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
   } else {
     epilogue_store<RB, RW, DV>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
   }
