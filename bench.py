@@ -28,8 +28,21 @@ def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+SETTLE_S = 0.25  # untimed back-to-back calls before the warmup, so the GPU clocks reach steady state
+
+
+def _settle(fn, seconds=SETTLE_S):
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def _time_calls(fn, steps, warmup):
     import torch
+    _settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
