@@ -220,6 +220,62 @@ struct TileIO {
     }
   }
 
+  // Two tiles of the same tokens (q and k of one block), rotated with shared
+  // sines and cosines, written as rows: dA / dB[t * ldr + col].
+  __device__ __forceinline__ static void commit_rows2(const TileIO &A, const TileIO &B, bool rot, long long p0,
+                                                      const float *theta_s, const float *rev_s, uint16_t *dA,
+                                                      uint16_t *dB, int ldr) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      if (idx >= ITEMS) continue;
+      int tg, c8;
+      item(idx, tg, c8);
+      float xa[TPT][8], xb[TPT][8];
+#pragma unroll
+      for (int r = 0; r < TPT; ++r) {
+        const uint32_t wa[4] = {A.raw[i][r].x, A.raw[i][r].y, A.raw[i][r].z, A.raw[i][r].w};
+        const uint32_t wb[4] = {B.raw[i][r].x, B.raw[i][r].y, B.raw[i][r].z, B.raw[i][r].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xa[r][2 * e] = __uint_as_float(wa[e] << 16);
+          xa[r][2 * e + 1] = __uint_as_float(wa[e] & 0xffff0000u);
+          xb[r][2 * e] = __uint_as_float(wb[e] << 16);
+          xb[r][2 * e + 1] = __uint_as_float(wb[e] & 0xffff0000u);
+        }
+      }
+      if (rot) {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const int pi = 4 * c8 + pp;
+          const float A0 = base_rev(p0 + TPT * tg, theta_s[pi]);
+          const float w = rev_s[pi];
+#pragma unroll
+          for (int r = 0; r < TPT; ++r) {
+            float rv = __builtin_fmaf((float)r, w, A0);
+            rv -= rintf(rv);
+            const float sn = __builtin_amdgcn_sinf(rv), c = __builtin_amdgcn_cosf(rv);
+            float re = xa[r][2 * pp], im = xa[r][2 * pp + 1];
+            xa[r][2 * pp] = re * c - im * sn;
+            xa[r][2 * pp + 1] = re * sn + im * c;
+            re = xb[r][2 * pp];
+            im = xb[r][2 * pp + 1];
+            xb[r][2 * pp] = re * c - im * sn;
+            xb[r][2 * pp + 1] = re * sn + im * c;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < TPT; ++r) {
+        uint16_t *ra = dA + (TPT * tg + r) * ldr + 8 * c8, *rb = dB + (TPT * tg + r) * ldr + 8 * c8;
+        *(u32x2 *)ra = u32x2{pack_bf2(xa[r][0], xa[r][1]), pack_bf2(xa[r][2], xa[r][3])};
+        *(u32x2 *)(ra + 4) = u32x2{pack_bf2(xa[r][4], xa[r][5]), pack_bf2(xa[r][6], xa[r][7])};
+        *(u32x2 *)rb = u32x2{pack_bf2(xb[r][0], xb[r][1]), pack_bf2(xb[r][2], xb[r][3])};
+        *(u32x2 *)(rb + 4) = u32x2{pack_bf2(xb[r][4], xb[r][5]), pack_bf2(xb[r][6], xb[r][7])};
+      }
+    }
+  }
+
   // rows:  dst[t * ldr + col]            (token-major, bf16; lo part to dstLo when LO)
   // trans: dstT[col * LDT + t] * zeta_t  (token-minor), zeta_t = gamma^(zoff - t) when `zeta`;
   //        with ZR instead dstT[t * ldz + col] * zeta_t (token-major, 16-byte stores, ldz % 8 == 0)
@@ -480,13 +536,12 @@ __device__ __forceinline__ void epilogue_groupnorm(const RetArgs &a, f32x4 (&ot)
 // Output of a 64-query block (bf16): the accumulators (after GroupNorm) go to
 // LDS as rows of O in the Os buffer (pitch DV + 8), then every store writes whole
 // 16-byte pieces of rows, coalesced across lanes; the gate, the inverse rotation
-// and the row reversal are applied in that row-wise pass.  Os must be free
-// (its readers done) on entry: the first barrier orders that.
+// and the row reversal are applied in that row-wise pass.  stage_out writes the
+// block to Os (which must be free); store_staged, after a barrier, does the row
+// pass.  epilogue_staged is the two with the barriers around them.
 template <int RB, int RW, int DV, bool PAIR>
-__device__ __forceinline__ void epilogue_staged(const RetArgs &a, f32x4 (&ot)[RB][4], uint16_t *Os, int b, int h,
-                                                int q0, int nvalid, long long obase, int w, int g, int l16) {
+__device__ __forceinline__ void stage_out(const f32x4 (&ot)[RB][4], uint16_t *Os, int w, int g, int l16) {
   constexpr int DVP = DV + 8;
-  __syncthreads();
 #pragma unroll
   for (int qb4 = 0; qb4 < 4; ++qb4) {
     const int row = 16 * qb4 + l16;
@@ -501,7 +556,12 @@ __device__ __forceinline__ void epilogue_staged(const RetArgs &a, f32x4 (&ot)[RB
             pack4(ot[rb][qb4][0], ot[rb][qb4][1], ot[rb][qb4][2], ot[rb][qb4][3]);
     }
   }
-  __syncthreads();
+}
+
+template <int DV>
+__device__ __forceinline__ void store_staged(const RetArgs &a, const uint16_t *Os, int b, int h, int q0, int nvalid,
+                                             long long obase) {
+  constexpr int DVP = DV + 8;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < BT * (DV / 8) / NT; ++i) {
@@ -532,6 +592,15 @@ __device__ __forceinline__ void epilogue_staged(const RetArgs &a, f32x4 (&ot)[RB
     const int n = a.out_rev ? a.L - 1 - (q0 + row) : q0 + row;
     __builtin_nontemporal_store(o, (u32x4 *)((uint16_t *)a.o + obase + (long long)n * a.o_sn + col));
   }
+}
+
+template <int RB, int RW, int DV, bool PAIR>
+__device__ __forceinline__ void epilogue_staged(const RetArgs &a, f32x4 (&ot)[RB][4], uint16_t *Os, int b, int h,
+                                                int q0, int nvalid, long long obase, int w, int g, int l16) {
+  __syncthreads();
+  stage_out<RB, RW, DV, PAIR>(ot, Os, w, g, l16);
+  __syncthreads();
+  store_staged<DV>(a, Os, b, h, q0, nvalid, obase);
 }
 
 template <int RB, int RW, int DV, bool PAIR = false>
@@ -872,6 +941,8 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
   }
 
   const int qblk = w & 3, kh = w >> 2;  // score split: 16 queries x 32 keys per wave
+  f32x4 ot[RB][4];
+  int out_q0 = -1, out_rows = 0;  // the block whose accumulators ot still holds
   for (int c0 = t_lo; c0 < t_hi; c0 += a.chunk) {
     const int Cc = min(a.chunk, a.L - c0);
     const bool carry = c0 + Cc < t_hi;  // state needed after this chunk
@@ -879,17 +950,28 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
     for (int qb = 0; qb < nqb_c; ++qb) {
       const int q0 = c0 + qb * BT;
       const bool last_qb = qb == nqb_c - 1;
+      // ---- block boundary: the previous block's output and this block's query
+      // (and, with resident keys, key) tiles share one pair of barriers
+      if (out_q0 >= 0 && !a.out_bf16) epilogue_store<RB, RW, DV, PAIR>(a, ot, red, b, h, out_q0, out_rows, obase, w, g, l16);
+      if (out_q0 >= 0 && a.out_bf16 && a.use_gn) epilogue_groupnorm<RB, DV>(a, ot, red, w, g, l16);
+      __syncthreads();  // readers of Vr, Qs/Kz, Ps and the resident slot qb are done
+      if (out_q0 >= 0 && a.out_bf16) {
+        static_assert(BT * (DV + 8) <= BT * LDV, "output staging fits in Vr");
+        stage_out<RB, RW, DV, PAIR>(ot, Vr, w, g, l16);
+      }
+      if constexpr (RES)  // q and k of the same tokens: one set of sines and cosines
+        TileIO<DK>::commit_rows2(qio, kio, rot, a.pos0 + q0, theta_s, rev_s, Qs, Ks + qb * BT * LDQ, LDQ);
+      else
+        qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, rev_s, Qs, LDQ, KsL, nullptr, false, 0.f,
+                                                0);
       __syncthreads();
-      qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, rev_s, Qs, LDQ, KsL, nullptr, false, 0.f,
-                                              0);
-      __syncthreads();
+      if (out_q0 >= 0 && a.out_bf16) store_staged<DV>(a, Vr, b, h, out_q0, out_rows, obase);
       u32x4 qreg[KS], qlo[SPLIT ? KS : 1];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         qreg[ks] = ld_op(Qs + (16 * qblk + l16) * LDQ, 32 * ks, g);
         if constexpr (SPLIT) qlo[ks] = ld_op(KsL + (16 * qblk + l16) * LDQ, 32 * ks, g);
       }
-      f32x4 ot[RB][4];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -929,18 +1011,20 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
         const float gdel = delta ? dpow(lg, 64 * (delta - 1)) : 1.0f;
         uint16_t *const Kb = RES ? Ks + kb * BT * LDQ : Ks;
         __syncthreads();
-        if (!RES || kb == qb) {
+        if constexpr (RES) {
+          if (upd) {  // zeta-scaled copy of the resident block for the update
+            TileIO<DK> kres;
+            kres.load_lds(Kb, LDQ);
+            kres.template commit<false, true, false, true>(false, 0, theta_s, rev_s, nullptr, LDQ, nullptr, Kz, true,
+                                                           lg, Cc - 1 - (k0 - c0), LDZ);
+          }
+        } else {
           if (upd)
             kio.template commit<true, true, SPLIT, true>(rot, a.pos0 + k0, theta_s, rev_s, Kb, LDQ, KsL, Kz, true,
                                                          lg, Cc - 1 - (k0 - c0), LDZ);
           else
             kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Kb, LDQ, KsL, nullptr, false,
                                                     0.f, 0);
-        } else if (upd) {  // resident block: zeta-scaled copy from LDS
-          TileIO<DK> kres;
-          kres.load_lds(Kb, LDQ);
-          kres.template commit<false, true, false, true>(false, 0, theta_s, rev_s, nullptr, LDQ, nullptr, Kz, true,
-                                                         lg, Cc - 1 - (k0 - c0), LDZ);
         }
         vio.template commit<false, false>(Vr, LDV, 0, theta_s, 0.0f, 0);
         __syncthreads();
@@ -954,21 +1038,16 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           nend = min(a.L, nk0 + a.chunk);
         }
         const bool has_next = nk0 < t_hi;
-        if constexpr (RES) {
-          // keys are needed from memory only at diagonal visits: the next one is
-          // the next query block's, and both tiles start at the same token
-          if (kb == qb) {
-            const int nq0 = last_qb ? nk0 : q0 + BT;
-            if (nq0 < t_hi) {
-              kio.fetch(k + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nend - nq0));
-              qio.fetch(q + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nend - nq0));
-            }
-          }
-        } else if (has_next) {
-          kio.fetch(k + (long long)nk0 * a.q_sn, a.q_sn, min(BT, nend - nk0));
-          if (kb == qb) {  // and the next query block's tile
-            const int nq0 = last_qb ? nk0 : q0 + BT;
+        if constexpr (!RES)
+          if (has_next) kio.fetch(k + (long long)nk0 * a.q_sn, a.q_sn, min(BT, nend - nk0));
+        // at the diagonal visit: the next block's query tile (and resident key
+        // tile), committed at the next block boundary.  Issued this late so the
+        // registers are free during the earlier visits.
+        if (kb == qb) {
+          const int nq0 = last_qb ? nk0 : q0 + BT;
+          if (nq0 < t_hi) {
             qio.fetch(q + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nend - nq0));
+            if constexpr (RES) kio.fetch(k + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nend - nq0));
           }
         }
 #pragma unroll
@@ -1013,15 +1092,17 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           }
         }
       }
-      if (a.out_bf16) {
-        // bf16 output staged through the V tile's LDS, free until the next visit's commit
-        static_assert(BT * (DV + 8) <= BT * LDV, "output staging fits in Vr");
-        if (a.use_gn) epilogue_groupnorm<RB, DV>(a, ot, red, w, g, l16);
-        epilogue_staged<RB, RW, DV, PAIR>(a, ot, Vr, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
-      } else {
-        epilogue_store<RB, RW, DV, PAIR>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
-      }
+      out_q0 = q0;
+      out_rows = min(BT, c0 + Cc - q0);
     }
+  }
+  // the last block's output
+  if (out_q0 < 0) return;
+  if (!a.out_bf16) {
+    epilogue_store<RB, RW, DV, PAIR>(a, ot, red, b, h, out_q0, out_rows, obase, w, g, l16);
+  } else {
+    if (a.use_gn) epilogue_groupnorm<RB, DV>(a, ot, red, w, g, l16);
+    epilogue_staged<RB, RW, DV, PAIR>(a, ot, Vr, b, h, out_q0, out_rows, obase, w, g, l16);
   }
 }
 
