@@ -561,15 +561,30 @@ __device__ __forceinline__ void stage_out(const f32x4 (&ot)[RB][4], uint16_t *Os
 template <int DV>
 __device__ __forceinline__ void store_staged(const RetArgs &a, const uint16_t *Os, int b, int h, int q0, int nvalid,
                                              long long obase) {
-  constexpr int DVP = DV + 8;
+  constexpr int DVP = DV + 8, C8 = DV / 8, NPT = BT * C8 / NT;  // 16-byte pieces per thread
+  static_assert(BT * C8 % NT == 0, "whole pieces per thread");
   const int tid = threadIdx.x;
+  // Stores go through a buffer resource covering the block's valid rows only
+  // (rows at or past nvalid fall outside it and are dropped by the hardware), so
+  // the pass has no branches.  With out_rev, row r goes to n = L-1-(q0+r): the
+  // resource starts at the lowest such n and offsets count down from it.
+  const long long nbase = a.out_rev ? (long long)a.L - q0 - nvalid : q0;
+  const int range = (int)((long long)nvalid * a.o_sn * 2);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)((uint16_t *)a.o + obase + nbase * a.o_sn), (short)0, range,
+                                        0x00020000);
+  u32x4 o[NPT];
 #pragma unroll
-  for (int i = 0; i < BT * (DV / 8) / NT; ++i) {
-    const int c = tid + NT * i, row = c / (DV / 8), col = 8 * (c % (DV / 8));
-    if (row >= nvalid) continue;
-    u32x4 o = *(const u32x4 *)(Os + row * DVP + col);
-    if (a.gate || a.out_rot) {
-      const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+  for (int i = 0; i < NPT; ++i) {
+    const int c = tid + NT * i;
+    o[i] = *(const u32x4 *)(Os + (c / C8) * DVP + 8 * (c % C8));
+  }
+  if (a.gate || a.out_rot) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int c = tid + NT * i, row = c / C8, col = 8 * (c % C8);
+      if (row >= nvalid) continue;
+      const uint32_t ow[4] = {o[i].x, o[i].y, o[i].z, o[i].w};
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -587,10 +602,16 @@ __device__ __forceinline__ void store_staged(const RetArgs &a, const uint16_t *O
         }
       }
       if (a.out_rot) unrotate_pairs<8>(a, x, a.pos0 + (a.out_rev ? a.L - 1 - (q0 + row) : q0 + row), col / 2);
-      o = u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
+      o[i] = u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
     }
-    const int n = a.out_rev ? a.L - 1 - (q0 + row) : q0 + row;
-    __builtin_nontemporal_store(o, (u32x4 *)((uint16_t *)a.o + obase + (long long)n * a.o_sn + col));
+  }
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int c = tid + NT * i, row = c / C8, col = 8 * (c % C8);
+    const long long n = a.out_rev ? (long long)nvalid - 1 - row : row;  // row index inside the resource
+    // rows past nvalid: offset at the end of the range -> every dword dropped
+    const int off = row < nvalid ? (int)((n * a.o_sn + col) * 2) : range;
+    __builtin_amdgcn_raw_buffer_store_b128(o[i], rs, off, 0, 2 /* slc: streaming */);
   }
 }
 
@@ -1027,7 +1048,9 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
                                                     0.f, 0);
         }
         vio.template commit<false, false>(Vr, LDV, 0, theta_s, 0.0f, 0);
-        __syncthreads();
+        // the scores read only the key block, which with resident keys was written
+        // at its block boundary: no barrier between these stores and the scores
+        if constexpr (!RES) __syncthreads();
         // next visit: next key block of this query block, else the first key block
         // of the next query block (of this chunk, or of the next chunk).  Its loads
         // are issued in two parts -- K before the scores, V before PV -- so the
