@@ -986,7 +986,9 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
         qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, rev_s, Qs, LDQ, KsL, nullptr, false, 0.f,
                                                 0);
       __syncthreads();
-      if (out_q0 >= 0 && a.out_bf16) store_staged<DV>(a, Vr, b, h, out_q0, out_rows, obase);
+      // unconditional (no rows when there is nothing staged), so that the stores
+      // and the cross-term MFMAs below share one basic block
+      store_staged<DV>(a, Vr, b, h, max(out_q0, 0), out_q0 >= 0 && a.out_bf16 ? out_rows : 0, obase);
       u32x4 qreg[KS], qlo[SPLIT ? KS : 1];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -1152,6 +1154,9 @@ struct BlockPos {
   __device__ __forceinline__ int valid() const { return min(BT, c0 + Cc - k0); }
 };
 
+#ifndef SS_NSET
+#define SS_NSET 2
+#endif
 template <int DK, int DVW>
 __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, float *seg_state, uint16_t *locT) {
   using T = Tile<DK, DVW>;
@@ -1182,22 +1187,24 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
   for (int dkb = 0; dkb < DKB; ++dkb)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  RowIO<DK> kio[2];
-  RowIO<DVW> vio[2];
+  // NSET register sets of global loads in flight (block i uses set i % NSET); two LDS buffers
+  constexpr int NSET = SS_NSET;
+  RowIO<DK> kio[NSET];
+  RowIO<DVW> vio[NSET];
   // pf: the next block to fetch; a block past the segment fetches no rows
   BlockPos cur{t_lo, t_lo, min(a.chunk, a.L - t_lo)}, pf = cur;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NSET; ++s) {
     const int nv = pf.k0 < t_hi ? pf.valid() : 0;
     kio[s].fetch(k + (long long)pf.k0 * a.q_sn, a.q_sn, nv);
     vio[s].fetch(v + (long long)pf.k0 * a.v_sn, a.v_sn, nv);
     pf.advance(a.L, a.chunk);
   }
   int buf = 0;
-  // two blocks per iteration, one per register set
+  // NSET blocks per iteration, one per register set
   for (bool more = true; more;) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < NSET; ++s) {
       if (cur.k0 >= t_hi) {
         more = false;
         break;
@@ -1229,7 +1236,7 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
         kio[s].template commit<false, true>(Kr[buf], LDK, 0, theta_s, lg, zoff);
       vio[s].template commit<false, false>(Vr[buf], LDV, 0, theta_s, 0.0f, 0);
       __syncthreads();
-      {  // this register set now takes the block two ahead
+      {  // this register set now takes the block NSET ahead
         const int nv = pf.k0 < t_hi ? pf.valid() : 0;
         kio[s].fetch(k + (long long)pf.k0 * a.q_sn, a.q_sn, nv);
         vio[s].fetch(v + (long long)pf.k0 * a.v_sn, a.v_sn, nv);
@@ -1278,7 +1285,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, 
     float4 *base = (float4 *)(ws + (long long)bh * geo.nseg * SZ);
     uint16_t *tb = sinT ? sinT + (long long)bh * geo.nseg * SZ : nullptr;
     const int row = (int)(4 * e / a.dv), col = (int)(4 * e % a.dv);  // element (dk row, dv col..col+3)
-    constexpr int SB = 8;  // segments whose loads are in flight together
+    constexpr int SB = 4;  // segments whose loads are in flight together
     for (int s0 = 0; s0 < geo.nseg; s0 += SB) {
       float4 d[SB];
 #pragma unroll
