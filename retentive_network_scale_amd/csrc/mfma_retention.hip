@@ -1154,9 +1154,6 @@ struct BlockPos {
   __device__ __forceinline__ int valid() const { return min(BT, c0 + Cc - k0); }
 };
 
-#ifndef SS_NSET
-#define SS_NSET 2
-#endif
 template <int DK, int DVW>
 __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, float *seg_state, uint16_t *locT) {
   using T = Tile<DK, DVW>;
@@ -1187,8 +1184,9 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
   for (int dkb = 0; dkb < DKB; ++dkb)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) st[dkb][rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // NSET register sets of global loads in flight (block i uses set i % NSET); two LDS buffers
-  constexpr int NSET = SS_NSET;
+  // NSET register sets of global loads in flight (block i uses set i % NSET; deeper
+  // sets measured no faster); two LDS buffers
+  constexpr int NSET = 2;
   RowIO<DK> kio[NSET];
   RowIO<DVW> vio[NSET];
   // pf: the next block to fetch; a block past the segment fetches no rows
