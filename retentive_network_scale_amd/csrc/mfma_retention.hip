@@ -99,13 +99,23 @@ __device__ __forceinline__ float dpow(float lg2, int d) {
   return d == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)d * lg2);
 }
 
-// Rotation table for a kernel: rev_s[i] = theta_i / (2 pi) in fp32, th_s[i] = theta_i.
-// A tile starting at absolute position P0 needs, per pair i, the fp64-reduced
-// base A_i = frac(P0 theta_i / 2pi); token t of the tile then has angle (in
-// revolutions) frac(A_i + t * rev_s[i]), t < 64, so the fp32 part stays small.
+// Rotation tables of a kernel: theta_s[i] = theta_i and step_s[i] = (cos theta_i,
+// sin theta_i) (libm, to an ulp).  A thread rotating consecutive tokens p0,
+// p0+1, ... of pair i takes the angle of the first from its fp64-reduced
+// revolutions, frac(p0 theta_i / 2pi), and the hardware v_cos/v_sin, then steps
+// to each next token by a complex multiplication with step_s[i]: a few fp32
+// roundings per token, far below the bf16 rounding of the result, and one
+// hardware sine/cosine pair per run of tokens instead of one per token.
 __device__ __forceinline__ float base_rev(long long p0, float theta) {
   double r = (double)p0 * (double)theta * 0.15915494309189535;
   return (float)(r - rint(r));
+}
+
+__device__ __forceinline__ void fill_rot_tables(const RetArgs &a, float *theta_s, float2 *step_s, int npairs) {
+  for (int i = threadIdx.x; i < npairs; i += blockDim.x) {
+    theta_s[i] = a.theta[i];
+    step_s[i] = make_float2(cosf(a.theta[i]), sinf(a.theta[i]));
+  }
 }
 
 // Decay table of one head in LDS: dt[x + 64] = gamma^x for 0 <= x < 128 and 0
@@ -223,7 +233,7 @@ struct TileIO {
   // Two tiles of the same tokens (q and k of one block), rotated with shared
   // sines and cosines, written as rows: dA / dB[t * ldr + col].
   __device__ __forceinline__ static void commit_rows2(const TileIO &A, const TileIO &B, bool rot, long long p0,
-                                                      const float *theta_s, const float *rev_s, uint16_t *dA,
+                                                      const float *theta_s, const float2 *step_s, uint16_t *dA,
                                                       uint16_t *dB, int ldr) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -249,12 +259,15 @@ struct TileIO {
         for (int pp = 0; pp < 4; ++pp) {
           const int pi = 4 * c8 + pp;
           const float A0 = base_rev(p0 + TPT * tg, theta_s[pi]);
-          const float w = rev_s[pi];
+          const float2 stp = step_s[pi];
+          float c = __builtin_amdgcn_cosf(A0), sn = __builtin_amdgcn_sinf(A0);
 #pragma unroll
           for (int r = 0; r < TPT; ++r) {
-            float rv = __builtin_fmaf((float)r, w, A0);
-            rv -= rintf(rv);
-            const float sn = __builtin_amdgcn_sinf(rv), c = __builtin_amdgcn_cosf(rv);
+            if (r > 0) {
+              const float c2 = c * stp.x - sn * stp.y;
+              sn = sn * stp.x + c * stp.y;
+              c = c2;
+            }
             float re = xa[r][2 * pp], im = xa[r][2 * pp + 1];
             xa[r][2 * pp] = re * c - im * sn;
             xa[r][2 * pp + 1] = re * sn + im * c;
@@ -281,7 +294,7 @@ struct TileIO {
   //        with ZR instead dstT[t * ldz + col] * zeta_t (token-major, 16-byte stores, ldz % 8 == 0)
   // Rotation (rot): token t of the tile sits at absolute position p0 + t.
   template <bool ROWS, bool TRANS, bool LO, bool ZR = false>
-  __device__ __forceinline__ void commit(bool rot, long long p0, const float *theta_s, const float *rev_s,
+  __device__ __forceinline__ void commit(bool rot, long long p0, const float *theta_s, const float2 *step_s,
                                          uint16_t *dst, int ldr, uint16_t *dstLo, uint16_t *dstT, bool zeta,
                                          float zlg, int zoff, int ldz = 0) const {
 #pragma unroll
@@ -305,12 +318,15 @@ struct TileIO {
         for (int pp = 0; pp < 4; ++pp) {
           const int pi = 4 * c8 + pp;
           const float A = base_rev(p0 + TPT * tg, theta_s[pi]);
-          const float w = rev_s[pi];
+          const float2 stp = step_s[pi];
+          float c = __builtin_amdgcn_cosf(A), sn = __builtin_amdgcn_sinf(A);
 #pragma unroll
           for (int r = 0; r < TPT; ++r) {
-            float rv = __builtin_fmaf((float)r, w, A);
-            rv -= rintf(rv);
-            const float sn = __builtin_amdgcn_sinf(rv), c = __builtin_amdgcn_cosf(rv);
+            if (r > 0) {
+              const float c2 = c * stp.x - sn * stp.y;
+              sn = sn * stp.x + c * stp.y;
+              c = c2;
+            }
             const float re = x[r][2 * pp], im = x[r][2 * pp + 1];
             x[r][2 * pp] = re * c - im * sn;
             x[r][2 * pp + 1] = re * sn + im * c;
@@ -718,7 +734,8 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   __shared__ __attribute__((aligned(16))) uint16_t KsL[SPLIT ? BT * LDQ : 8];
   __shared__ __attribute__((aligned(16))) uint16_t Vr[BT * LDV];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[BT * LDT];
-  __shared__ float theta_s[DK / 2], rev_s[DK / 2];
+  __shared__ float theta_s[DK / 2];
+  __shared__ float2 step_s[DK / 2];
   __shared__ float red[8][BT];
   __shared__ float dt[DT_SZ];
   uint16_t *const Qs = Ks;
@@ -748,11 +765,7 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   const uint16_t *k = (const uint16_t *)a.k + (long long)b * a.q_sb + (long long)h * a.q_sh;
   const uint16_t *v = (const uint16_t *)a.v + (long long)b * a.v_sb + (long long)h * a.v_sh;
   const long long obase = (long long)b * a.o_sb + (long long)h * a.o_sh;
-  if (rot)
-    for (int i = tid; i < DK / 2; i += NT) {
-      theta_s[i] = a.theta[i];
-      rev_s[i] = (float)((double)a.theta[i] * 0.15915494309189535);
-    }
+  if (rot) fill_rot_tables(a, theta_s, step_s, DK / 2);
   fill_decay_table(dt, lg, NT);
 
   TileIO<DK> qio, kio;
@@ -761,7 +774,7 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   kio.fetch(k + (long long)c0 * a.q_sn, a.q_sn, min(BT, Cc));
   vio.fetch(v + (long long)c0 * a.v_sn, a.v_sn, min(BT, Cc));
   __syncthreads();
-  qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, rev_s, Qs, LDQ, KsL, nullptr, false, 0.f, 0);
+  qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, step_s, Qs, LDQ, KsL, nullptr, false, 0.f, 0);
   __syncthreads();
   const int qblk = w & 3, kh = w >> 2;  // score split: 16 queries x 32 keys per wave
   u32x4 qreg[KS], qlo[SPLIT ? KS : 1];
@@ -827,7 +840,7 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
     const int delta = qb - kb;
     const float gdel = delta ? dpow(lg, 64 * (delta - 1)) : 1.0f;
     __syncthreads();
-    kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Ks, LDQ, KsL, nullptr, false, 0.f, 0);
+    kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, step_s, Ks, LDQ, KsL, nullptr, false, 0.f, 0);
     vio.template commit<false, false>(Vr, LDV, 0, theta_s, 0.0f, 0);
     __syncthreads();
     if (kb < qb) {
@@ -914,7 +927,8 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
   __shared__ __attribute__((aligned(16))) uint16_t Ps[BT * LDT];
   uint16_t *const Qs = QKs;
   uint16_t *const Kz = QKs;
-  __shared__ float theta_s[DK / 2], rev_s[DK / 2];
+  __shared__ float theta_s[DK / 2];
+  __shared__ float2 step_s[DK / 2];
   __shared__ float red[8][BT];
   __shared__ float dt[DT_SZ];
 
@@ -930,11 +944,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
   const uint16_t *k = (const uint16_t *)a.k + (long long)b * a.q_sb + (long long)h * a.q_sh;
   const uint16_t *v = (const uint16_t *)a.v + (long long)b * a.v_sb + (long long)h * a.v_sh;
   const long long obase = (long long)b * a.o_sb + (long long)h * a.o_sh;
-  if (rot)
-    for (int i = tid; i < DK / 2; i += NT) {
-      theta_s[i] = a.theta[i];
-      rev_s[i] = (float)((double)a.theta[i] * 0.15915494309189535);
-    }
+  if (rot) fill_rot_tables(a, theta_s, step_s, DK / 2);
   fill_decay_table(dt, lg, NT);
 
   // fp32 state in D layout: st[dkb][rb][i] = S[16dkb+4g+i][w*RW+16rb+l16]
@@ -981,9 +991,9 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
         stage_out<RB, RW, DV, PAIR>(ot, Vr, w, g, l16);
       }
       if constexpr (RES)  // q and k of the same tokens: one set of sines and cosines
-        TileIO<DK>::commit_rows2(qio, kio, rot, a.pos0 + q0, theta_s, rev_s, Qs, Ks + qb * BT * LDQ, LDQ);
+        TileIO<DK>::commit_rows2(qio, kio, rot, a.pos0 + q0, theta_s, step_s, Qs, Ks + qb * BT * LDQ, LDQ);
       else
-        qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, rev_s, Qs, LDQ, KsL, nullptr, false, 0.f,
+        qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, step_s, Qs, LDQ, KsL, nullptr, false, 0.f,
                                                 0);
       __syncthreads();
       // unconditional (no rows when there is nothing staged), so that the stores
@@ -1038,15 +1048,15 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           if (upd) {  // zeta-scaled copy of the resident block for the update
             TileIO<DK> kres;
             kres.load_lds(Kb, LDQ);
-            kres.template commit<false, true, false, true>(false, 0, theta_s, rev_s, nullptr, LDQ, nullptr, Kz, true,
+            kres.template commit<false, true, false, true>(false, 0, theta_s, step_s, nullptr, LDQ, nullptr, Kz, true,
                                                            lg, Cc - 1 - (k0 - c0), LDZ);
           }
         } else {
           if (upd)
-            kio.template commit<true, true, SPLIT, true>(rot, a.pos0 + k0, theta_s, rev_s, Kb, LDQ, KsL, Kz, true,
+            kio.template commit<true, true, SPLIT, true>(rot, a.pos0 + k0, theta_s, step_s, Kb, LDQ, KsL, Kz, true,
                                                          lg, Cc - 1 - (k0 - c0), LDZ);
           else
-            kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, rev_s, Kb, LDQ, KsL, nullptr, false,
+            kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, step_s, Kb, LDQ, KsL, nullptr, false,
                                                     0.f, 0);
         }
         vio.template commit<false, false>(Vr, LDV, 0, theta_s, 0.0f, 0);
