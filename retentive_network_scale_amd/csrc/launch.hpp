@@ -32,7 +32,6 @@ struct ChunkPlan {
   int nseg;           // segments per (b, h)
   size_t seg_bytes;   // fp32 segment states [B*H][nseg][dk][dv]
   size_t sinT_bytes;  // bf16 incoming segment states, transposed [B*H][nseg][dv][dk]
-  size_t loc_bytes;   // bf16 local chunk states, transposed [B*H][nchunks][dv][dk]
   size_t ws_bytes;    // total
 };
 ChunkPlan chunk_plan(int B, int H, int L, int dk, int dv, int chunk);

@@ -715,8 +715,8 @@ __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB]
 // ---------------------------------------------------------------- query-block kernel
 // One task = (b, h, chunk c, 64-query block qb).  PAR: the parallel form (one
 // chunk spanning the sequence, no cross term).  Otherwise the chunkwise output
-// with the incoming state S_c = gamma^(c0-s0) S_in(segment) + local(c), both
-// stored bf16 as S^T[dv][dk] (SinT per segment, locT per chunk).
+// with the state entering chunk c, S_c, stored bf16 as S_c^T[dv][dk] in SinT
+// (every chunk is a segment of its own on this path).
 // SPLIT: scores from hi + lo bf16 parts of the rotated q and k (three MFMAs per
 // k-step), accurate to ~2^-16 instead of the ~2^-8 of one bf16 rounding of the
 // rotated values.  Used when GroupNorm follows: rows whose variance is near eps
@@ -724,8 +724,7 @@ __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB]
 // The global loads of the next key block are issued right after the current
 // one is committed to LDS, so they are in flight during the MFMA work.
 template <int DK, int DV, bool PAR, bool SPLIT>
-__global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, const uint16_t *SinT,
-                                                    const uint16_t *locT) {
+__global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, const uint16_t *SinT) {
   using T = Tile<DK, DV>;
   constexpr int LDQ = T::LDQ, RW = T::RW, RB = T::RB, KS = T::KS;
   constexpr int LDV = tr_pitch(DV);  // token-major V tile, read across rows (ld_op_tr)
@@ -790,42 +789,26 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
 #pragma unroll
     for (int qb4 = 0; qb4 < 4; ++qb4) ot[rb][qb4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (!PAR) {
-    // cross term gamma^(j+1) q S_c.  A operand rows: S_c^T[w*RW + 16rb + l16][dk K-set]
-    const int seg = c / geo.seg_chunks;
-    const int s0 = seg * geo.seg_chunks * a.chunk;
-    const bool has_loc = c % geo.seg_chunks != 0;
-    const float gs = dpow(lg, c0 - s0);
-    const uint16_t *sin_t = SinT + ((long long)bh * geo.nseg + seg) * DK * DV;
-    const uint16_t *loc_t = locT + ((long long)bh * geo.nchunks + c) * DK * DV;
+    // cross term gamma^(j+1) q S_c.  A operand rows: S_c^T[w*RW + 16rb + l16][dk];
+    // inside each 32-wide k-step lane group g takes k = 8g..8g+7 (for both
+    // operands), so every A load is 16 contiguous bytes straight from memory.
+    // The loads of step ks+1 are issued before the MFMAs of step ks.
+    const uint16_t *s_t = SinT + ((long long)bh * geo.nchunks + c) * DK * DV + (long long)(w * RW + l16) * DK + 8 * g;
+    u32x4 sa[2][RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sa[0][rb] = *(const u32x4 *)(s_t + 16 * rb * DK);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 as[RB];
+      if (ks + 1 < KS)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const long long off = (long long)(w * RW + 16 * rb + l16) * DK + 32 * ks + 4 * g;
-        const u32x2 s_lo = *(const u32x2 *)(sin_t + off), s_hi = *(const u32x2 *)(sin_t + off + 16);
-        const uint32_t sw[4] = {s_lo.x, s_lo.y, s_hi.x, s_hi.y};
-        uint32_t aw[4];
-        if (has_loc) {
-          const u32x2 l_lo = *(const u32x2 *)(loc_t + off), l_hi = *(const u32x2 *)(loc_t + off + 16);
-          const uint32_t lw[4] = {l_lo.x, l_lo.y, l_hi.x, l_hi.y};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            aw[e] = pack_bf2(__builtin_fmaf(gs, __uint_as_float(sw[e] << 16), __uint_as_float(lw[e] << 16)),
-                             __builtin_fmaf(gs, __uint_as_float(sw[e] & 0xffff0000u),
-                                            __uint_as_float(lw[e] & 0xffff0000u)));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            aw[e] = pack_bf2(gs * __uint_as_float(sw[e] << 16), gs * __uint_as_float(sw[e] & 0xffff0000u));
-        }
-        as[rb] = u32x4{aw[0], aw[1], aw[2], aw[3]};
-      }
+        for (int rb = 0; rb < RB; ++rb) sa[(ks + 1) & 1][rb] = *(const u32x4 *)(s_t + 16 * rb * DK + 32 * (ks + 1));
 #pragma unroll
       for (int qb4 = 0; qb4 < 4; ++qb4) {
-        const u32x4 bq = ld_op(Qs + (16 * qb4 + l16) * LDQ, 32 * ks, g);
+        const uint16_t *qr = Qs + (16 * qb4 + l16) * LDQ + 32 * ks + 8 * g;
+        const u32x2 lo = *(const u32x2 *)qr, hi = *(const u32x2 *)(qr + 4);
+        const u32x4 bq = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = mfma(as[rb], bq, ot[rb][qb4]);
+        for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = mfma(sa[ks & 1][rb], bq, ot[rb][qb4]);
       }
     }
 #pragma unroll
@@ -1145,10 +1128,8 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
 // Walks the segment chunk by chunk from a zero state:
 //   S <- gamma^Cc S + sum_i gamma^(Cc-1-i) k_i^T v_i     (per chunk)
 // 64 tokens at a time, double-buffered in LDS, with the global loads of the
-// next two blocks in flight (two register sets, used alternately).  Before
-// every chunk after the first it stores S (the local state entering that
-// chunk) as bf16 S^T[dv][dk] in locT; at the end it stores the segment's own
-// state (fp32, [dk][dv]) in seg_state.
+// next two blocks in flight (two register sets, used alternately).  At the end
+// it stores the segment's own state (fp32, [dk][dv]) in seg_state.
 
 // Position of a 64-token block: its first token, and its chunk's start and length.
 struct BlockPos {
@@ -1165,7 +1146,7 @@ struct BlockPos {
 };
 
 template <int DK, int DVW>
-__global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, float *seg_state, uint16_t *locT) {
+__global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, float *seg_state) {
   using T = Tile<DK, DVW>;
   constexpr int RW = T::RW, RB = T::RB, DKB = T::DKB;
   constexpr int LDK = tr_pitch(DK), LDV = tr_pitch(DVW);
@@ -1218,17 +1199,7 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
         break;
       }
       if (cur.k0 == cur.c0 && cur.c0 > t_lo) {
-        // local state entering this chunk -> locT (bf16, S^T[dv][dk]) when
-        // requested; then decay it over the chunk
-        if (locT) {
-          uint16_t *dst = locT + ((long long)bh * geo.nchunks + cur.c0 / a.chunk) * DK * a.dv;
-#pragma unroll
-          for (int dkb = 0; dkb < DKB; ++dkb)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              *(u32x2 *)(dst + (long long)(split * DVW + w * RW + 16 * rb + l16) * DK + 16 * dkb + 4 * g) =
-                  pack4(st[dkb][rb][0], st[dkb][rb][1], st[dkb][rb][2], st[dkb][rb][3]);
-        }
+        // a new chunk of the segment: decay the state over it
         const float gc = dpow(lg, cur.Cc);
 #pragma unroll
         for (int dkb = 0; dkb < DKB; ++dkb)
@@ -1277,11 +1248,12 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
 }
 
 // ---------------------------------------------------------------- pass 2: scan over segments
-// In place: ws[bh][s] holds the segment's own state on entry and the state
-// entering segment s on exit; sinT[bh][s] receives the same as bf16
-// S^T[dv][dk].  Also writes the state after the last token.
-__global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, float *ws, uint16_t *sinT,
-                                                       const float *state_in, float *state_out) {
+// Exclusive scan over a (b, h)'s segments of S <- gamma^len S + S_own(segment).
+// seg_scan_kernel (state kept in registers by the output kernel): in place,
+// ws[bh][s] holds the segment's own state on entry and the state entering
+// segment s on exit.  Both write the state after the last token.
+__global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, float *ws, const float *state_in,
+                                                       float *state_out) {
   const long long SZ = (long long)a.dk * a.dv;
   const long long n4 = SZ / 4;
   const int bh = blockIdx.y;
@@ -1291,8 +1263,6 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, 
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += (long long)gridDim.x * blockDim.x) {
     float4 run = state_in ? ((const float4 *)(state_in + (long long)bh * SZ))[e] : make_float4(0.f, 0.f, 0.f, 0.f);
     float4 *base = (float4 *)(ws + (long long)bh * geo.nseg * SZ);
-    uint16_t *tb = sinT ? sinT + (long long)bh * geo.nseg * SZ : nullptr;
-    const int row = (int)(4 * e / a.dv), col = (int)(4 * e % a.dv);  // element (dk row, dv col..col+3)
     constexpr int SB = 4;  // segments whose loads are in flight together
     for (int s0 = 0; s0 < geo.nseg; s0 += SB) {
       float4 d[SB];
@@ -1304,13 +1274,6 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, 
         const int s = s0 + j;
         if (s >= geo.nseg) break;
         base[(long long)s * n4 + e] = run;
-        if (sinT) {
-          uint16_t *t = tb + (long long)s * SZ + row;
-          t[(long long)(col + 0) * a.dk] = f2bf(run.x);
-          t[(long long)(col + 1) * a.dk] = f2bf(run.y);
-          t[(long long)(col + 2) * a.dk] = f2bf(run.z);
-          t[(long long)(col + 3) * a.dk] = f2bf(run.w);
-        }
         const int len = min(a.L, (s + 1) * seg_len) - s * seg_len;
         const float gm = len == seg_len ? g_full : dpow(lg, len);
         run.x = gm * run.x + d[j].x;
@@ -1321,6 +1284,76 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, 
     }
     if (state_out) ((float4 *)(state_out + (long long)bh * SZ))[e] = run;
   }
+}
+
+// seg_scan_t_kernel (states handed to the query-block kernel): the state
+// entering segment s goes to sinT[bh][s] as bf16 S^T[dv][dk] only.  One block
+// per 64 x 64 tile of (dk, dv): each thread scans four float4s of the tile
+// (coalesced loads of ws[bh][s]); the transposition goes through LDS so that
+// every store writes 16 contiguous bytes of a dv row.
+__global__ __launch_bounds__(256) void seg_scan_t_kernel(RetArgs a, TaskGeom geo, const float *ws, uint16_t *sinT,
+                                                         const float *state_in, float *state_out) {
+  constexpr int TP = 64 + 8;  // LDS pitch (bf16) of the transposed tile
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * TP];
+  const long long SZ = (long long)a.dk * a.dv;
+  const int bh = blockIdx.y;
+  const int ntc = a.dv / 64;  // tiles along dv
+  const int r0 = 64 * (blockIdx.x / ntc), c0 = 64 * (blockIdx.x % ntc);
+  const int t = threadIdx.x, tr = t / 16, tc = 4 * (t % 16);  // rows tr + 16j, columns tc..tc+3
+  const float lg = safe_log2(a.gamma[bh % a.H]);
+  const int seg_len = geo.seg_chunks * a.chunk;
+  const float g_full = dpow(lg, seg_len);
+  float4 run[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    run[j] = state_in ? *(const float4 *)(state_in + bh * SZ + (long long)(r0 + tr + 16 * j) * a.dv + c0 + tc)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float *base = ws + (long long)bh * geo.nseg * SZ;
+  uint16_t *tb = sinT + (long long)bh * geo.nseg * SZ;
+  float4 d[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) d[j] = *(const float4 *)(base + (long long)(r0 + tr + 16 * j) * a.dv + c0 + tc);
+  for (int s = 0; s < geo.nseg; ++s) {
+    // tile[col][row] = bf16(run): thread's column tc+i, rows tr+16j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = tr + 16 * j;
+      tile[(tc + 0) * TP + row] = f2bf(run[j].x);
+      tile[(tc + 1) * TP + row] = f2bf(run[j].y);
+      tile[(tc + 2) * TP + row] = f2bf(run[j].z);
+      tile[(tc + 3) * TP + row] = f2bf(run[j].w);
+    }
+    const int len = min(a.L, (s + 1) * seg_len) - s * seg_len;
+    const float gm = len == seg_len ? g_full : dpow(lg, len);
+    float4 dn[4];
+    if (s + 1 < geo.nseg)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dn[j] = *(const float4 *)(base + (long long)(s + 1) * SZ + (long long)(r0 + tr + 16 * j) * a.dv + c0 + tc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      run[j].x = gm * run[j].x + d[j].x;
+      run[j].y = gm * run[j].y + d[j].y;
+      run[j].z = gm * run[j].z + d[j].z;
+      run[j].w = gm * run[j].w + d[j].w;
+      d[j] = dn[j];
+    }
+    __syncthreads();
+    // 64 dv rows x 64 dk (128 bytes): two 16-byte pieces per thread
+    uint16_t *dst = tb + (long long)s * SZ;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int pc = t + 256 * i, col = pc / 8, piece = pc % 8;
+      const uint16_t *src = tile + col * TP + 8 * piece;
+      const u32x2 lo = *(const u32x2 *)src, hi = *(const u32x2 *)(src + 4);
+      *(u32x4 *)(dst + (long long)(c0 + col) * a.dk + r0 + 8 * piece) = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+    __syncthreads();
+  }
+  if (state_out)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(float4 *)(state_out + bh * SZ + (long long)(r0 + tr + 16 * j) * a.dv + c0 + tc) = run[j];
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -1342,26 +1375,25 @@ ChunkPlan chunk_plan(int B, int H, int L, int dk, int dv, int chunk) {
   const int nsplit = dv / state_dvw(dk, dv);
   const int nchunks = (L + chunk - 1) / chunk;
   const int units = B * H * nsplit;
+  // states that fit one workgroup's accumulators stay in registers through a
+  // segment; larger ones are handed to the query-block kernel as the bf16 state
+  // entering every chunk, so there every chunk is a segment of its own
+  const bool in_regs = nsplit == 1;
   const int target = 256;  // segment-state pass: about one workgroup per CU
-  int nseg = (target + units - 1) / units;
+  int nseg = in_regs ? (target + units - 1) / units : nchunks;
   if (nseg > nchunks) nseg = nchunks;
   if (nseg < 1) nseg = 1;
   p.seg_chunks = (nchunks + nseg - 1) / nseg;
   p.nseg = (nchunks + p.seg_chunks - 1) / p.seg_chunks;
   const size_t SZ = (size_t)dk * dv;
   p.seg_bytes = (size_t)B * H * p.nseg * SZ * sizeof(float);
-  // states that fit one workgroup's accumulators stay in registers through a
-  // segment; larger ones are stored per chunk (bf16) for the query-block kernel
-  const bool in_regs = nsplit == 1;
   p.sinT_bytes = in_regs ? 0 : (size_t)B * H * p.nseg * SZ * 2;
-  p.loc_bytes = in_regs ? 0 : (size_t)B * H * nchunks * SZ * 2;
-  p.ws_bytes = p.seg_bytes + p.sinT_bytes + p.loc_bytes;
+  p.ws_bytes = p.seg_bytes + p.sinT_bytes;
   return p;
 }
 
 template <int DK, int DV>
-static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const uint16_t *sinT, const uint16_t *locT,
-                              hipStream_t st) {
+static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const uint16_t *sinT, hipStream_t st) {
   geo.nqb = par ? (a.L + BT - 1) / BT : (a.chunk + BT - 1) / BT;
   geo.nchunks = par ? 1 : (a.L + a.chunk - 1) / a.chunk;
   geo.ntasks = a.B * a.H * geo.nchunks * geo.nqb;
@@ -1378,16 +1410,16 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
     g2.sel = 2;
     const dim3 grid1(xcd_grid(g1.ntasks));
     if (par) {
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid1, dim3(NT), 0, st, a, g1, sinT, locT);
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, g2, sinT, locT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid1, dim3(NT), 0, st, a, g1, sinT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, g2, sinT);
     } else {
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid1, dim3(NT), 0, st, a, g1, sinT, locT);
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, g2, sinT, locT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid1, dim3(NT), 0, st, a, g1, sinT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, g2, sinT);
     }
   } else if (par) {
-    hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, sinT, locT);
+    hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, sinT);
   } else {
-    hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, sinT, locT);
+    hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, sinT);
   }
   return hipGetLastError();
 }
@@ -1399,15 +1431,20 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
   constexpr bool IN_REGS = DVW1 == DV;
   float *seg = (float *)ws;
   uint16_t *sinT = IN_REGS ? nullptr : (uint16_t *)(ws + p.seg_bytes);
-  uint16_t *locT = IN_REGS ? nullptr : (uint16_t *)(ws + p.seg_bytes + p.sinT_bytes);
   TaskGeom geo{p.nseg, p.seg_chunks, DV / DVW1, 1, 0, (a.L + a.chunk - 1) / a.chunk};
   geo.ntasks = a.B * a.H * geo.nseg * geo.nsplit;
-  hipLaunchKernelGGL((seg_state_kernel<DK, DVW1>), dim3(xcd_grid(geo.ntasks)), dim3(NT), 0, st, a, geo, seg, locT);
+  hipLaunchKernelGGL((seg_state_kernel<DK, DVW1>), dim3(xcd_grid(geo.ntasks)), dim3(NT), 0, st, a, geo, seg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long n4 = (long long)a.dk * a.dv / 4;
-  hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)((n4 + 255) / 256), a.B * a.H), dim3(256), 0, st, a, geo, seg,
-                     sinT, state_in, state_out);
+  if constexpr (IN_REGS) {
+    const long long n4 = (long long)a.dk * a.dv / 4;
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)((n4 + 255) / 256), a.B * a.H), dim3(256), 0, st, a, geo, seg,
+                       state_in, state_out);
+  } else {
+    static_assert(DK % 64 == 0 && DV % 64 == 0, "64 x 64 scan tiles");
+    hipLaunchKernelGGL(seg_scan_t_kernel, dim3((DK / 64) * (DV / 64), a.B * a.H), dim3(256), 0, st, a, geo, seg, sinT,
+                       state_in, state_out);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (IN_REGS) {
@@ -1421,18 +1458,18 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
       hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, seg);
     return hipGetLastError();
   } else {
-    return run_qblocks<DK, DV>(a, geo, false, sinT, locT, st);
+    return run_qblocks<DK, DV>(a, geo, false, sinT, st);
   }
 }
 
 hipError_t launch_mfma_parallel(const RetArgs &a, hipStream_t st) {
   TaskGeom geo{1, 1, 1, 1, 0, 1};
-  if (a.dk == 64 && a.dv == 128) return run_qblocks<64, 128>(a, geo, true, nullptr, nullptr, st);
-  if (a.dk == 128 && a.dv == 128) return run_qblocks<128, 128>(a, geo, true, nullptr, nullptr, st);
-  if (a.dk == 128 && a.dv == 256) return run_qblocks<128, 256>(a, geo, true, nullptr, nullptr, st);
-  if (a.dk == 256 && a.dv == 128) return run_qblocks<256, 128>(a, geo, true, nullptr, nullptr, st);
-  if (a.dk == 256 && a.dv == 256) return run_qblocks<256, 256>(a, geo, true, nullptr, nullptr, st);
-  if (a.dk == 256 && a.dv == 512) return run_qblocks<256, 512>(a, geo, true, nullptr, nullptr, st);
+  if (a.dk == 64 && a.dv == 128) return run_qblocks<64, 128>(a, geo, true, nullptr, st);
+  if (a.dk == 128 && a.dv == 128) return run_qblocks<128, 128>(a, geo, true, nullptr, st);
+  if (a.dk == 128 && a.dv == 256) return run_qblocks<128, 256>(a, geo, true, nullptr, st);
+  if (a.dk == 256 && a.dv == 128) return run_qblocks<256, 128>(a, geo, true, nullptr, st);
+  if (a.dk == 256 && a.dv == 256) return run_qblocks<256, 256>(a, geo, true, nullptr, st);
+  if (a.dk == 256 && a.dv == 512) return run_qblocks<256, 512>(a, geo, true, nullptr, st);
   return hipErrorNotSupported;
 }
 
