@@ -1364,9 +1364,16 @@ bool mfma_supported(int dk, int dv) {
 
 // dv columns per workgroup in the segment-state pass: the fp32 state slice
 // DK x DVW lives in the accumulators of 8 waves (<= 64 registers each).
+// States of up to 128 x 256 fp32 stay in the output kernel's accumulators (eight
+// waves, 64 registers each) through a segment.  Larger ones go to the
+// query-block kernel; their segment-state pass holds up to 256 x 256 (128
+// registers per lane) and splits d_v beyond that (each split re-reads K).
+constexpr long long IN_REGS_MAX = 128 * 256, SPLIT_STATE_MAX = 256 * 256;
+static bool state_in_regs(int dk, int dv) { return (long long)dk * dv <= IN_REGS_MAX; }
 static int state_dvw(int dk, int dv) {
+  if (state_in_regs(dk, dv)) return dv;
   int dvw = dv;
-  while ((long long)dk * dvw > 128 * 256) dvw /= 2;
+  while ((long long)dk * dvw > SPLIT_STATE_MAX) dvw /= 2;
   return dvw;
 }
 
@@ -1378,7 +1385,7 @@ ChunkPlan chunk_plan(int B, int H, int L, int dk, int dv, int chunk) {
   // states that fit one workgroup's accumulators stay in registers through a
   // segment; larger ones are handed to the query-block kernel as the bf16 state
   // entering every chunk, so there every chunk is a segment of its own
-  const bool in_regs = nsplit == 1;
+  const bool in_regs = state_in_regs(dk, dv);
   const int target = 256;  // segment-state pass: about one workgroup per CU
   int nseg = in_regs ? (target + units - 1) / units : nchunks;
   if (nseg > nchunks) nseg = nchunks;
@@ -1427,8 +1434,8 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
 template <int DK, int DV>
 static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, const float *state_in,
                                 float *state_out, hipStream_t st) {
-  constexpr int DVW1 = (DK * DV > 128 * 256) ? (128 * 256) / DK : DV;
-  constexpr bool IN_REGS = DVW1 == DV;
+  constexpr bool IN_REGS = (long long)DK * DV <= IN_REGS_MAX;
+  constexpr int DVW1 = IN_REGS ? DV : (DK * DV > SPLIT_STATE_MAX ? (int)(SPLIT_STATE_MAX / DK) : DV);
   float *seg = (float *)ws;
   uint16_t *sinT = IN_REGS ? nullptr : (uint16_t *)(ws + p.seg_bytes);
   TaskGeom geo{p.nseg, p.seg_chunks, DV / DVW1, 1, 0, (a.L + a.chunk - 1) / a.chunk};
