@@ -40,6 +40,9 @@
 //      cross term, converted to bf16).
 // The parallel form is the query-block kernel: one task per (b, h, 64-query
 // block), key blocks up to the diagonal, no state.
+#include <map>
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -1399,6 +1402,36 @@ ChunkPlan chunk_plan(int B, int H, int L, int dk, int dv, int chunk) {
   return p;
 }
 
+// A second stream per device (default priority) on which a small launch can run
+// beside the main one: fork from and join back to the caller's stream with
+// events.  The events are shared, so the fork/launch/join sequence is done under
+// a mutex; graph capture follows the fork into the side stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+
+static SideStream *side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  static std::mutex mu;
+  static std::map<int, SideStream *> per_dev;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = per_dev.find(dev);
+  if (it != per_dev.end()) return it->second;
+  SideStream *ss = new SideStream;
+  if (hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    delete ss;  // (handles that were created are kept by the runtime until exit)
+    ss = nullptr;
+  }
+  per_dev[dev] = ss;
+  return ss;
+}
+
 template <int DK, int DV>
 static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const uint16_t *sinT, hipStream_t st) {
   geo.nqb = par ? (a.L + BT - 1) / BT : (a.chunk + BT - 1) / BT;
@@ -1416,13 +1449,33 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
     g1.ntasks = a.B * a.H;
     g2.sel = 2;
     const dim3 grid1(xcd_grid(g1.ntasks));
+    // chunkwise: the first blocks (one small launch) run on the side stream,
+    // beside the rest (measured no faster for the parallel form, whose first
+    // blocks take a single short visit)
+    SideStream *ss = par ? nullptr : side_stream();
+    std::unique_lock<std::mutex> lock;
+    hipStream_t st1 = st;
+    if (ss) {
+      lock = std::unique_lock<std::mutex>(ss->mu);
+      if (hipEventRecord(ss->fork, st) == hipSuccess && hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess)
+        st1 = ss->s;
+      else
+        (void)hipGetLastError();
+    }
     if (par) {
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid1, dim3(NT), 0, st, a, g1, sinT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid1, dim3(NT), 0, st1, a, g1, sinT);
       hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, g2, sinT);
     } else {
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid1, dim3(NT), 0, st, a, g1, sinT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid1, dim3(NT), 0, st1, a, g1, sinT);
       hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, g2, sinT);
     }
+    hipError_t e = hipGetLastError();
+    if (st1 != st) {
+      const hipError_t ej = hipEventRecord(ss->join, st1) == hipSuccess ? hipStreamWaitEvent(st, ss->join, 0)
+                                                                         : hipGetLastError();
+      if (e == hipSuccess) e = ej;
+    }
+    return e;
   } else if (par) {
     hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, sinT);
   } else {

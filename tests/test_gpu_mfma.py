@@ -132,3 +132,37 @@ def test_gamma_edges_mfma():
     _tol.assert_bf16(rn.retention_parallel(qd, kd, vd, g, out_dtype=torch.float32), ref, what="parallel")
     o, _ = rn.retention_chunkwise(qd, kd, vd, g, 64, out_dtype=torch.float32)
     _tol.assert_bf16(o, ref, what="chunkwise")
+
+
+def test_chunkwise_gn_rot_graph_replay():
+    """The chunkwise path for large states with GroupNorm and rotation runs its
+    hi+lo first query blocks on a second stream forked from the caller's and
+    joined back.  Captured in a graph and replayed with new inputs, eager work
+    and synchronisations between replays: every replay equals the eager call on
+    the same inputs, bit for bit."""
+    B, H, L, dk, dv, chunk = 2, 2, 320, 256, 512, 128
+    g, th = multiscale_gamma(H), rotation_theta(dk)
+    inputs = [_gpu(*_qkv(B, H, L, dk, dv, 700 + 10 * i)) for i in range(3)]
+    wsb = rn.retention_chunkwise_workspace_bytes(B, H, L, dk, dv, chunk)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    eager = [rn.retention_chunkwise(q, k, v, g, chunk, th, gn_eps=1e-5, workspace=ws)[0] for q, k, v in inputs]
+    qs, ks, vs = (torch.empty_like(t) for t in inputs[0])
+    out = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        rn.retention_chunkwise(qs, ks, vs, g, chunk, th, gn_eps=1e-5, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rn.retention_chunkwise(qs, ks, vs, g, chunk, th, gn_eps=1e-5, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for i, (q, k, v) in enumerate(inputs):
+        qs.copy_(q)
+        ks.copy_(k)
+        vs.copy_(v)
+        _ = (q.float() * 2).sum()  # unrelated eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[i]), f"replay {i} differs from the eager call"
