@@ -558,9 +558,18 @@ __device__ __forceinline__ void epilogue_groupnorm(const RetArgs &a, f32x4 (&ot)
 // and the row reversal are applied in that row-wise pass.  stage_out writes the
 // block to Os (which must be free); store_staged, after a barrier, does the row
 // pass.  epilogue_staged is the two with the barriers around them.
-template <int RB, int RW, int DV, bool PAIR>
+// Staging addresses: row pitch DV + 8 (SW false), or DV with the 16-byte chunks
+// of row r stored at chunk index c ^ (r & 7) (SW: the block fills a 64 x DV
+// buffer exactly; 8-byte stores of 16 rows then meet at most two per bank).
+template <int DV, bool SW>
+__device__ __forceinline__ int stage_idx(int row, int col) {
+  return SW ? row * DV + (((col >> 3) ^ (row & 7)) << 3) + (col & 7) : row * (DV + 8) + col;
+}
+
+template <int RB, int RW, int DV, bool PAIR, bool SW = false>
 __device__ __forceinline__ void stage_out(const f32x4 (&ot)[RB][4], uint16_t *Os, int w, int g, int l16) {
   constexpr int DVP = DV + 8;
+  static_assert(!(PAIR && SW), "paired order is staged unswizzled");
 #pragma unroll
   for (int qb4 = 0; qb4 < 4; ++qb4) {
     const int row = 16 * qb4 + l16;
@@ -571,16 +580,16 @@ __device__ __forceinline__ void stage_out(const f32x4 (&ot)[RB][4], uint16_t *Os
     } else {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        *(u32x2 *)(Os + row * DVP + w * RW + 16 * rb + 4 * g) =
+        *(u32x2 *)(Os + stage_idx<DV, SW>(row, w * RW + 16 * rb + 4 * g)) =
             pack4(ot[rb][qb4][0], ot[rb][qb4][1], ot[rb][qb4][2], ot[rb][qb4][3]);
     }
   }
 }
 
-template <int DV>
+template <int DV, bool SW = false>
 __device__ __forceinline__ void store_staged(const RetArgs &a, const uint16_t *Os, int b, int h, int q0, int nvalid,
                                              long long obase) {
-  constexpr int DVP = DV + 8, C8 = DV / 8, NPT = BT * C8 / NT;  // 16-byte pieces per thread
+  constexpr int C8 = DV / 8, NPT = BT * C8 / NT;  // 16-byte pieces per thread
   static_assert(BT * C8 % NT == 0, "whole pieces per thread");
   const int tid = threadIdx.x;
   // Stores go through a buffer resource covering the block's valid rows only
@@ -596,7 +605,7 @@ __device__ __forceinline__ void store_staged(const RetArgs &a, const uint16_t *O
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
     const int c = tid + NT * i;
-    o[i] = *(const u32x4 *)(Os + (c / C8) * DVP + 8 * (c % C8));
+    o[i] = *(const u32x4 *)(Os + stage_idx<DV, SW>(c / C8, 8 * (c % C8)));
   }
   if (a.gate || a.out_rot) {
 #pragma unroll
@@ -715,6 +724,60 @@ __device__ __forceinline__ void epilogue_store(const RetArgs &a, f32x4 (&ot)[RB]
   }
 }
 
+// ---------------------------------------------------------------- V tiles by LDS-DMA
+// A V tile (64 token rows of DV bf16) stored unpadded, the 16-byte chunks of
+// row r at chunk index c ^ vswz(r), which makes the transposed operand reads
+// (ld_op_trs) conflict-free.  It is filled by LDS-DMA loads (buffer_load ...
+// lds): wave instruction J of the tile writes LDS bytes [1024 J, 1024 J + 1024),
+// lane l the 16 bytes at 1024 J + 16 l, fetched from whichever global chunk
+// belongs there.  Rows at or past `valid` read as zero (range-checked resource).
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+
+template <int DV>
+__device__ __forceinline__ void v_dma(uint16_t *Vb, const uint16_t *src, long long v_sn, int valid) {
+  constexpr int RBYTES = DV * 2, NJ = BT * RBYTES / 1024 / (NT / 64);  // instructions per wave
+  static_assert(BT * RBYTES % (1024 * (NT / 64)) == 0, "whole instructions per wave");
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int nbytes = valid > 0 ? (int)((long long)valid * v_sn * 2) : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nbytes, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int J = w * NJ + j, off = J * 1024 + 16 * l;
+    const int row = off / RBYTES, c = ((off % RBYTES) >> 4) ^ vswz(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(Vb + J * 512), 16,
+                                             (int)(row * v_sn * 2) + 16 * c, 0, 0, 0);
+  }
+}
+
+// ld_op_tr on a V tile in that layout: rows k0 + 4g + p/4 (+16), columns
+// m0 + 4(p%4) (m0 % 16 == 0), i.e. chunk m0/8 + (p%4)/2, half p%2.
+template <int DV>
+__device__ __forceinline__ u32x4 ld_op_trs(const uint16_t *Vb, int k0, int m0, int g, int l16) {
+  const int row = k0 + 4 * g + (l16 >> 2);
+  const int c = (m0 >> 3) + ((l16 & 3) >> 1);
+  const uint16_t *p0 = Vb + row * DV + ((c ^ vswz(row)) << 3) + 4 * (l16 & 1);
+  const tr_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr_v4s *)p0);
+  const tr_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr_v4s *)(p0 + 16 * DV));
+  const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l.x, l.y, h.x, h.y};
+}
+
+// Waits for this wave's outstanding vector-memory operations, LDS-DMA loads
+// included (s_waitcnt vmcnt(0)).  A DMA-filled tile is read by other waves, so
+// every wave calls this before the barrier that publishes the tile.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier that publishes LDS stores only: waits for this wave's LDS
+// operations (lgkmcnt(0)) but not for outstanding global loads or LDS-DMA, which
+// stay in flight across it (__syncthreads would wait for those too).  The
+// signal fences keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------- query-block kernel
 // One task = (b, h, chunk c, 64-query block qb).  PAR: the parallel form (one
 // chunk spanning the sequence, no cross term).  Otherwise the chunkwise output
@@ -730,11 +793,10 @@ template <int DK, int DV, bool PAR, bool SPLIT>
 __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, const uint16_t *SinT) {
   using T = Tile<DK, DV>;
   constexpr int LDQ = T::LDQ, RW = T::RW, RB = T::RB, KS = T::KS;
-  constexpr int LDV = tr_pitch(DV);  // token-major V tile, read across rows (ld_op_tr)
   // The query block is staged through Ks / KsL (free until the key loop starts).
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BT * LDQ];
   __shared__ __attribute__((aligned(16))) uint16_t KsL[SPLIT ? BT * LDQ : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Vr[BT * LDV];
+  __shared__ __attribute__((aligned(16))) uint16_t Vb[BT * DV];  // V tile (LDS-DMA, swizzled)
   __shared__ __attribute__((aligned(16))) uint16_t Ps[BT * LDT];
   __shared__ float theta_s[DK / 2];
   __shared__ float2 step_s[DK / 2];
@@ -771,10 +833,8 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   fill_decay_table(dt, lg, NT);
 
   TileIO<DK> qio, kio;
-  RowIO<DV> vio;
   qio.fetch(q + (long long)q0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - q0));
   kio.fetch(k + (long long)c0 * a.q_sn, a.q_sn, min(BT, Cc));
-  vio.fetch(v + (long long)c0 * a.v_sn, a.v_sn, min(BT, Cc));
   __syncthreads();
   qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, step_s, Qs, LDQ, KsL, nullptr, false, 0.f, 0);
   __syncthreads();
@@ -826,14 +886,10 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
     const int delta = qb - kb;
     const float gdel = delta ? dpow(lg, 64 * (delta - 1)) : 1.0f;
     __syncthreads();
+    // this visit's V tile streams into LDS during the key commit and the scores
+    v_dma<DV>(Vb, v + (long long)k0 * a.v_sn, a.v_sn, min(BT, c0 + Cc - k0));
     kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, step_s, Ks, LDQ, KsL, nullptr, false, 0.f, 0);
-    vio.template commit<false, false>(Vr, LDV, 0, theta_s, 0.0f, 0);
-    __syncthreads();
-    if (kb < qb) {
-      const int n0 = k0 + BT;
-      kio.fetch(k + (long long)n0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - n0));
-      vio.fetch(v + (long long)n0 * a.v_sn, a.v_sn, min(BT, c0 + Cc - n0));
-    }
+    lds_barrier();  // the keys; the V tile stays in flight
     // scores S^T[key][query] for keys 32kh..+32, queries 16qblk..+16; decay, mask, -> Ps
 #pragma unroll
     for (int kb16 = 0; kb16 < 2; ++kb16) {
@@ -854,13 +910,18 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
       for (int i = 0; i < 4; ++i) p[i] = sc[i] * (gdel * dt[dp - i]);
       *(u32x2 *)(Ps + (16 * qblk + l16) * LDT + 32 * kh + 16 * kb16 + 4 * g) = pack4(p[0], p[1], p[2], p[3]);
     }
+    wait_vmem();  // this wave's part of the V tile has landed; the barrier publishes all of it
     __syncthreads();
+    if (kb < qb) {  // the next visit's keys, in flight during the P.V products
+      const int n0 = k0 + BT;
+      kio.fetch(k + (long long)n0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - n0));
+    }
     // O^T += V^T P^T
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 av[RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) av[rb] = ld_op_tr(Vr, LDV, 32 * ks, w * RW + 16 * rb, g, l16);
+      for (int rb = 0; rb < RB; ++rb) av[rb] = ld_op_trs<DV>(Vb, 32 * ks, w * RW + 16 * rb, g, l16);
 #pragma unroll
       for (int qb4 = 0; qb4 < 4; ++qb4) {
         const u32x4 bp = ld_op(Ps + (16 * qb4 + l16) * LDT, 32 * ks, g);
@@ -869,10 +930,12 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
       }
     }
   }
-  if (a.out_bf16) {  // staged through the V tile's LDS, free after the last visit
-    static_assert(BT * (DV + 8) <= BT * LDV, "output staging fits in Vr");
+  if (a.out_bf16) {  // staged (swizzled) through the V tile's LDS, free after the last visit
     if (a.use_gn) epilogue_groupnorm<RB, DV>(a, ot, red, w, g, l16);
-    epilogue_staged<RB, RW, DV, false>(a, ot, Vr, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
+    __syncthreads();
+    stage_out<RB, RW, DV, false, true>(ot, Vb, w, g, l16);
+    __syncthreads();
+    store_staged<DV, true>(a, Vb, b, h, q0, min(BT, c0 + Cc - q0), obase);
   } else {
     epilogue_store<RB, RW, DV>(a, ot, red, b, h, q0, min(BT, c0 + Cc - q0), obase, w, g, l16);
   }
