@@ -172,12 +172,15 @@ BwdPlan bwd_plan(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_t in_
 // writing the gradient `out` directly: on the MFMA kernels the epilogue applies
 // the inverse rotation (out_rot) and the token reversal (out_rev); on the vector
 // path the result goes through fp32 scratch and a separate pass.
+// in_rev (MFMA path, states kept in registers): the retention reads q, k and v
+// in reversed token order itself, so no reversed copies are needed.
 hipError_t bwd_retention(const void *q, const void *k, const void *v, void *out, float *scratch, int B, int H, int L,
                          int dqk, int dvv, int chunk, const float *gamma, const float *theta, long long pos0,
                          bool out_rot, bool out_rev, ret_dtype_t in_dtype, ret_dtype_t out_dtype, void *cws,
-                         hipStream_t st) {
+                         hipStream_t st, bool in_rev = false) {
   if (use_mfma(dqk, dvv, in_dtype)) {
     RetArgs a = make_args(q, k, v, out, B, H, L, dqk, dvv, chunk, gamma, nullptr, pos0, -1.0f, in_dtype, out_dtype);
+    a.in_rev = in_rev;
     a.out_rev = out_rev;
     a.out_rot = out_rot && theta;
     if (a.out_rot)
@@ -335,17 +338,32 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
   hipStream_t st = (hipStream_t)hip_stream;
   char *ws = (char *)workspace;
   RetArgs th = make_args(q, k, v, dq, B, H, L, dk, dv, chunk, gamma, theta, pos0, -1.0f, in_dtype, out_dtype);
-  const bool rot = theta != nullptr, bf = in_dtype == RET_BF16, obf = out_dtype == RET_BF16;
+  const bool rot = theta != nullptr, bf = in_dtype == RET_BF16;
   const long long rows = (long long)B * H * L;  // token rows of every tensor
   hipError_t e;
+  float *dqr = (float *)(ws + p.dq), *dkr = (float *)(ws + p.dk), *dvr = (float *)(ws + p.dv);
+  void *cws = ws + p.cws;
+  if (use_mfma(dk, dv, in_dtype) && use_mfma(dv, dk, in_dtype) && (long long)dk * dv <= 128 * 256) {
+    // the MFMA kernels read the reversed sequences themselves: only the rotated
+    // keys and queries are prepared (forward order; the p.kr and p.qrev slots)
+    void *kr = ws + p.kr, *qr = ws + p.qrev;
+    if ((e = launch_bwd_prep(k, kr, nullptr, rows, L, dk, rot, pos0, bf, th, st)) != hipSuccess ||
+        (e = launch_bwd_prep(q, qr, nullptr, rows, L, dk, rot, pos0, bf, th, st)) != hipSuccess ||
+        (e = bwd_retention(d_o, v, kr, dq, dqr, B, H, L, dv, dk, chunk, gamma, theta, pos0, true, false, in_dtype,
+                           out_dtype, cws, st)) != hipSuccess ||
+        (e = bwd_retention(v, d_o, qr, dk_out, dkr, B, H, L, dv, dk, chunk, gamma, theta, pos0, true, true, in_dtype,
+                           out_dtype, cws, st, true)) != hipSuccess ||
+        (e = bwd_retention(kr, qr, d_o, dv_out, dvr, B, H, L, dk, dv, chunk, gamma, nullptr, pos0, false, true,
+                           in_dtype, out_dtype, cws, st, true)) != hipSuccess)
+      return hip_status(e);
+    return ok();
+  }
   // rotated keys (forward and reversed), rotated queries (reversed), reversed V and dO
   if ((e = launch_bwd_prep(k, ws + p.kr, ws + p.krev, rows, L, dk, rot, pos0, bf, th, st)) != hipSuccess ||
       (e = launch_bwd_prep(q, nullptr, ws + p.qrev, rows, L, dk, rot, pos0, bf, th, st)) != hipSuccess ||
       (e = launch_bwd_prep(v, nullptr, ws + p.vrev, rows, L, dv, false, 0, bf, th, st)) != hipSuccess ||
       (e = launch_bwd_prep(d_o, nullptr, ws + p.dorev, rows, L, dv, false, 0, bf, th, st)) != hipSuccess)
     return hip_status(e);
-  float *dqr = (float *)(ws + p.dq), *dkr = (float *)(ws + p.dk), *dvr = (float *)(ws + p.dv);
-  void *cws = ws + p.cws;
   if ((e = bwd_retention(d_o, v, ws + p.kr, dq, dqr, B, H, L, dv, dk, chunk, gamma, theta, pos0, true, false,
                          in_dtype, out_dtype, cws, st)) != hipSuccess ||
       (e = bwd_retention(ws + p.vrev, ws + p.dorev, ws + p.qrev, dk_out, dkr, B, H, L, dv, dk, chunk, gamma, theta,

@@ -24,6 +24,9 @@ struct RetArgs {
   // sits at position p by exp(-i p theta_i) (theta from this struct, p = pos0 +
   // the row's index after any reversal).
   int out_rev, out_rot;
+  // Input reversal (segment-state and segment-output kernels, no rotation): the
+  // kernels' token n is row L-1-n of q, k and v
+  int in_rev;
   long long q_sb, q_sh, q_sn;
   long long v_sb, v_sh, v_sn;
   long long o_sb, o_sh, o_sn;

@@ -173,8 +173,10 @@ struct TileIO {
 
   // Buffer loads through a resource whose range ends after row valid-1: rows at
   // or past `valid` read as zero (hardware range check), with no branches and
-  // 32-bit offsets.  Rows are `stride` elements apart.
-  __device__ __forceinline__ void fetch(const uint16_t *src, long long stride, int valid) {
+  // 32-bit offsets.  Rows are `stride` elements apart.  rev: tile row t is row
+  // valid-1-t of src (rows past `valid` then have negative offsets, which the
+  // range check also rejects).
+  __device__ __forceinline__ void fetch(const uint16_t *src, long long stride, int valid, bool rev = false) {
     const int nbytes = valid > 0 ? (int)((long long)valid * stride * 2) : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nbytes, 0x00020000);
 #pragma unroll
@@ -184,33 +186,14 @@ struct TileIO {
       item(idx, tg, c8);
 #pragma unroll
       for (int r = 0; r < TPT; ++r) {
-        const int off = ((TPT * tg + r) * (int)stride + 8 * c8) * 2;
+        const int row = rev ? valid - 1 - (TPT * tg + r) : TPT * tg + r;
+        const int off = (row * (int)stride + 8 * c8) * 2;
         if (ITEMS % NT == 0 || idx < ITEMS) {
           const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
           raw[i][r] = make_uint4(x.x, x.y, x.z, x.w);
         } else {
           raw[i][r] = make_uint4(0u, 0u, 0u, 0u);
         }
-      }
-    }
-  }
-
-  // The loads of fetch() for token slot r only (fetch == fetch_row for r = 0..TPT-1),
-  // so that a tile's loads can be spread between other instructions.
-  __device__ __forceinline__ void fetch_row(const uint16_t *src, long long stride, int valid, int r) {
-    const int nbytes = valid > 0 ? (int)((long long)valid * stride * 2) : 0;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nbytes, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int idx = threadIdx.x + NT * i;
-      int tg, c8;
-      item(idx, tg, c8);
-      const int off = ((TPT * tg + r) * (int)stride + 8 * c8) * 2;
-      if (ITEMS % NT == 0 || idx < ITEMS) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        raw[i][r] = make_uint4(x.x, x.y, x.z, x.w);
-      } else {
-        raw[i][r] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
   }
@@ -406,13 +389,15 @@ struct RowIO {
   static_assert(ITEMS % NT == 0, "whole items per thread");
   uint4 raw[NI];
 
-  __device__ __forceinline__ void fetch(const uint16_t *src, long long stride, int valid) {
+  // as TileIO::fetch, rev included
+  __device__ __forceinline__ void fetch(const uint16_t *src, long long stride, int valid, bool rev = false) {
     const int nbytes = valid > 0 ? (int)((long long)valid * stride * 2) : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nbytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int idx = threadIdx.x + NT * i, t = idx / C8, c8 = idx % C8;
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, (t * (int)stride + 8 * c8) * 2, 0, 0);
+      const int row = rev ? valid - 1 - t : t;
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, (row * (int)stride + 8 * c8) * 2, 0, 0);
       raw[i] = make_uint4(x.x, x.y, x.z, x.w);
     }
   }
@@ -456,6 +441,14 @@ struct RowIO {
     }
   }
 };
+
+// First row of the tile [k0, k0 + valid) of a sequence in memory.  With in_rev
+// the kernel's token n is row L-1-n of the tensor, so the tile is rows
+// [L - k0 - valid, L - k0), fetched bottom-up (fetch(..., rev = true)).
+__device__ __forceinline__ const uint16_t *tile_src(const uint16_t *seq, long long k0, int valid, long long sn,
+                                                    const RetArgs &a) {
+  return seq + (a.in_rev ? (long long)a.L - k0 - valid : k0) * sn;
+}
 
 struct TaskGeom {
   int nseg, seg_chunks, nsplit, nqb, ntasks;
@@ -1015,9 +1008,9 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
   RowIO<DV> vio;
   {
     const int Cc = min(a.chunk, a.L - t_lo);
-    qio.fetch(q + (long long)t_lo * a.q_sn, a.q_sn, min(BT, Cc));
-    kio.fetch(k + (long long)t_lo * a.q_sn, a.q_sn, min(BT, Cc));
-    vio.fetch(v + (long long)t_lo * a.v_sn, a.v_sn, min(BT, Cc));
+    qio.fetch(tile_src(q, t_lo, min(BT, Cc), a.q_sn, a), a.q_sn, min(BT, Cc), a.in_rev);
+    kio.fetch(tile_src(k, t_lo, min(BT, Cc), a.q_sn, a), a.q_sn, min(BT, Cc), a.in_rev);
+    vio.fetch(tile_src(v, t_lo, min(BT, Cc), a.v_sn, a), a.v_sn, min(BT, Cc), a.in_rev);
   }
 
   const int qblk = w & 3, kh = w >> 2;  // score split: 16 queries x 32 keys per wave
@@ -1123,15 +1116,16 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
         }
         const bool has_next = nk0 < t_hi;
         if constexpr (!RES)
-          if (has_next) kio.fetch(k + (long long)nk0 * a.q_sn, a.q_sn, min(BT, nend - nk0));
+          if (has_next) kio.fetch(tile_src(k, nk0, min(BT, nend - nk0), a.q_sn, a), a.q_sn, min(BT, nend - nk0), a.in_rev);
         // at the diagonal visit: the next block's query tile (and resident key
         // tile), committed at the next block boundary.  Issued this late so the
         // registers are free during the earlier visits.
         if (kb == qb) {
           const int nq0 = last_qb ? nk0 : q0 + BT;
           if (nq0 < t_hi) {
-            qio.fetch(q + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nend - nq0));
-            if constexpr (RES) kio.fetch(k + (long long)nq0 * a.q_sn, a.q_sn, min(BT, nend - nq0));
+            qio.fetch(tile_src(q, nq0, min(BT, nend - nq0), a.q_sn, a), a.q_sn, min(BT, nend - nq0), a.in_rev);
+            if constexpr (RES)
+              kio.fetch(tile_src(k, nq0, min(BT, nend - nq0), a.q_sn, a), a.q_sn, min(BT, nend - nq0), a.in_rev);
           }
         }
 #pragma unroll
@@ -1152,7 +1146,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           for (int i = 0; i < 4; ++i) p[i] = sc[i] * (gdel * dt[dp - i]);
           *(u32x2 *)(Ps + (16 * qblk + l16) * LDT + 32 * kh + 16 * kb16 + 4 * g) = pack4(p[0], p[1], p[2], p[3]);
         }
-        if (has_next) vio.fetch(v + (long long)nk0 * a.v_sn, a.v_sn, min(BT, nend - nk0));
+        if (has_next) vio.fetch(tile_src(v, nk0, min(BT, nend - nk0), a.v_sn, a), a.v_sn, min(BT, nend - nk0), a.in_rev);
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -1251,8 +1245,8 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
 #pragma unroll
   for (int s = 0; s < NSET; ++s) {
     const int nv = pf.k0 < t_hi ? pf.valid() : 0;
-    kio[s].fetch(k + (long long)pf.k0 * a.q_sn, a.q_sn, nv);
-    vio[s].fetch(v + (long long)pf.k0 * a.v_sn, a.v_sn, nv);
+    kio[s].fetch(tile_src(k, pf.k0, nv, a.q_sn, a), a.q_sn, nv, a.in_rev);
+    vio[s].fetch(tile_src(v, pf.k0, nv, a.v_sn, a), a.v_sn, nv, a.in_rev);
     pf.advance(a.L, a.chunk);
   }
   int buf = 0;
@@ -1283,8 +1277,8 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
       __syncthreads();
       {  // this register set now takes the block NSET ahead
         const int nv = pf.k0 < t_hi ? pf.valid() : 0;
-        kio[s].fetch(k + (long long)pf.k0 * a.q_sn, a.q_sn, nv);
-        vio[s].fetch(v + (long long)pf.k0 * a.v_sn, a.v_sn, nv);
+        kio[s].fetch(tile_src(k, pf.k0, nv, a.q_sn, a), a.q_sn, nv, a.in_rev);
+        vio[s].fetch(tile_src(v, pf.k0, nv, a.v_sn, a), a.v_sn, nv, a.in_rev);
         pf.advance(a.L, a.chunk);
       }
 #pragma unroll
