@@ -280,11 +280,13 @@ def copy_calibration(reps=3):
 
 
 # Which dispatches make one call of each workload, for the PMC summary:
-# (kernels summed per call, kernel that occurs once per call).
+# (kernels summed per call, kernel that occurs exactly once per call).  The
+# parallel form launches two query-block kernels per call (its hi+lo first
+# blocks, SPLIT = true, and the rest): only the second counts the calls.
 _PMC_GROUPS = {
-    "chunkwise_32k": ("ret::", ("seg_out_kernel", "qblock_kernel")),
+    "chunkwise_32k": ("ret::", ("seg_out_kernel",)),
     "decode_step": ("vec_step_kernel", ("vec_step_kernel",)),
-    "parallel_2k": ("qblock_kernel", ("qblock_kernel",)),
+    "parallel_2k": ("qblock_kernel", ("qblock_kernel<256, 512, true, false>",)),
 }
 
 
