@@ -33,16 +33,21 @@ def test_backward_fp32(L, chunk, pos0, rot):
         _tol.assert_fp32(a, b, slice_dims=2, what=f"d{name}")
 
 
-@pytest.mark.parametrize("dk,dv,L,chunk", [(128, 256, 300, 64), (128, 256, 513, 256), (64, 128, 200, 100),
-                                           (128, 128, 260, 128)])
-def test_backward_bf16(dk, dv, L, chunk):
+@pytest.mark.parametrize("dk,dv,L,chunk,rot,pos0", [(128, 256, 300, 64, True, 3), (128, 256, 513, 256, True, 3),
+                                                     (64, 128, 200, 100, True, 3), (128, 128, 260, 128, True, 3),
+                                                     (64, 128, 130, 64, False, 0),
+                                                     (128, 256, 200, 64, True, 100000)])
+def test_backward_bf16(dk, dv, L, chunk, rot, pos0):
+    """bf16 inputs on the MFMA kernels, which rotate on load (value rows at their
+    own positions, reversed queries and keys by -theta): with and without
+    rotation, and at a large starting position."""
     B, H = 1, 4
     q, k, v, do = _inputs(B, H, L, dk, dv, 1200 + dk + L, torch.bfloat16)
-    g, th = multiscale_gamma(H), rotation_theta(dk)
-    got = rn.retention_chunkwise_bwd(*(t.to(DEV) for t in (q, k, v, do)), g, chunk, th, pos0=3,
+    g, th = multiscale_gamma(H), (rotation_theta(dk) if rot else None)
+    got = rn.retention_chunkwise_bwd(*(t.to(DEV) for t in (q, k, v, do)), g, chunk, th, pos0=pos0,
                                      out_dtype=torch.float32)
     torch.cuda.synchronize()
-    ref = oracle.backward(q, k, v, do, g, th, 3)
+    ref = oracle.backward(q, k, v, do, g, th, pos0)
     for name, a, b in zip("qkv", got, ref):
         _tol.assert_bf16(a, b, slice_dims=2, what=f"d{name}")
 
