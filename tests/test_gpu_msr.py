@@ -41,6 +41,39 @@ def test_msr_layer_small(B, L, dm, H, dk, dv, chunk):
     _tol.assert_bf16(y, ref, slice_dims=1, what="msr layer per batch")
 
 
+def test_msr_layer_graph_replay():
+    """The whole layer (hipBLASLt GEMMs, the chunkwise passes, the query-block
+    kernel's first blocks on a second stream forked from the caller's and joined
+    back) captured in a graph and replayed with new inputs, with eager work and
+    synchronisations between replays: every replay equals the eager call on the
+    same inputs, bit for bit."""
+    B, L, dm, H, dk, dv, chunk = 1, 256, 512, 2, 256, 512, 128
+    g, th = multiscale_gamma(H), rotation_theta(dk)
+    _, w = _inputs(B, L, dm, H, dk, dv, 640)
+    wd = [t.to(DEV) for t in w]
+    xs_in = [randn((B, L, dm), 650 + i, 1.0, torch.bfloat16).to(DEV) for i in range(3)]
+    ws = torch.empty(rn.msr_layer_fwd_workspace_bytes(B, L, dm, H, dk, dv, chunk), dtype=torch.uint8, device=DEV)
+    eager = [rn.msr_layer_fwd(x, *wd, H, dk, dv, chunk, g, th, workspace=ws).clone() for x in xs_in]
+    xs = torch.empty_like(xs_in[0])
+    out = torch.empty_like(xs_in[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream (library plans are built here)
+        rn.msr_layer_fwd(xs, *wd, H, dk, dv, chunk, g, th, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rn.msr_layer_fwd(xs, *wd, H, dk, dv, chunk, g, th, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for i, x in enumerate(xs_in):
+        xs.copy_(x)
+        _ = (x.float() * 2).sum()  # unrelated eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[i]), f"replay {i} differs from the eager call"
+
+
 def test_msr_zero_gate():
     """W_G = 0 gives swish(0) = 0 and an all-zero output."""
     B, L, dm, H, dk, dv = 1, 130, 256, 2, 64, 128
