@@ -290,7 +290,7 @@ _PMC_GROUPS = {
 }
 
 
-def pmc_summary(name, fetch_csv, write_csv, command):
+def pmc_summary(name, fetch_csv, write_csv, command, out_dir=None):
     """Turns two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then
     WRITE_SIZE, in KiB per dispatch) of a `bench.py --only ... --copy-calibration`
     run into profiles/traffic_<name>.txt: HBM bytes per call, scaled by the
@@ -318,7 +318,7 @@ def pmc_summary(name, fetch_csv, write_csv, command):
     hbm = f_kib * 1024 * f_fac + w_kib * 1024 * w_fac
     alg = {"chunkwise_32k": _alg_bytes_chunkwise(), "decode_step": _alg_bytes_decode(),
            "parallel_2k": _alg_bytes_parallel()}[name]
-    out = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{name}.txt")
     with open(out, "w") as fh:
         fh.write(f"# HBM traffic per call of {name}: rocprofv3 PMC FETCH_SIZE and WRITE_SIZE (KiB per dispatch),\n"
                  f"# summed over the dispatches of one call ({calls} calls), each scaled by the factor that maps\n"
