@@ -1489,12 +1489,32 @@ static SideStream *side_stream() {
   return ss;
 }
 
+// Scores from hi + lo bf16 parts of the rotated q and k for every block: when
+// rotation is on and some head decays fast (gamma < 0.75), its rows sum fewer
+// than about (1 + gamma) / (1 - gamma) < 7 effective terms, so the rounding of
+// the rotated values to bf16 (relative 2^-9 per element, which cancels only
+// in exact arithmetic) would not average out (at gamma = 0 every row is one
+// score times one value row).  Unrotated bf16 operands multiply exactly.
+static bool split_all_blocks(const RetArgs &a) {
+  if (!a.use_theta) return false;
+  for (int h = 0; h < a.H; ++h)
+    if (a.gamma[h] < 0.75f) return true;
+  return false;
+}
+
 template <int DK, int DV>
 static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const uint16_t *sinT, hipStream_t st) {
   geo.nqb = par ? (a.L + BT - 1) / BT : (a.chunk + BT - 1) / BT;
   geo.nchunks = par ? 1 : (a.L + a.chunk - 1) / a.chunk;
   geo.ntasks = a.B * a.H * geo.nchunks * geo.nqb;
   const dim3 grid(xcd_grid(geo.ntasks));
+  if (split_all_blocks(a)) {
+    if (par)
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid, dim3(NT), 0, st, a, geo, sinT);
+    else
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid, dim3(NT), 0, st, a, geo, sinT);
+    return hipGetLastError();
+  }
   if (a.use_gn && a.use_theta) {
     // Under GroupNorm a row whose output variance is near eps is divided by
     // about sqrt(eps), which magnifies the rounding of the rotated q and k to
@@ -1567,7 +1587,7 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
   if constexpr (IN_REGS) {
     geo.ntasks = a.B * a.H * geo.nseg;
     const dim3 grid(xcd_grid(geo.ntasks));
-    if (a.use_gn && a.use_theta)
+    if ((a.use_gn && a.use_theta) || split_all_blocks(a))
       hipLaunchKernelGGL((seg_out_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, seg);
     else if (DK <= 128 && a.chunk <= KRES * BT)  // resident keys fit in LDS for DK <= 128
       hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, (DK <= 128)>), grid, dim3(NT), 0, st, a, geo, seg);
