@@ -1,10 +1,11 @@
-"""Seeded random sweep of the bf16 MFMA path against the fp64 oracle ("Retentive
-Network" paper summary, Sec. 2.1 and 2.2): each case draws a head-size pair,
-batch, heads, a ragged length, a chunk size, per-head decays (including the
-edges 0 and 1), a starting position up to 2^31, rotation and GroupNorm on or
-off, the output dtype and an incoming state, then checks the chunkwise form
-(output and final state, against the recurrent oracle) and the parallel form
-(against the parallel oracle) at the bf16 bar."""
+"""Seeded random sweeps against the fp64 oracle ("Retentive Network" paper
+summary, Sec. 2.1 and 2.2).  Each case draws its shapes (head sizes, batch,
+heads, a ragged length, a chunk size), per-head decays (including the edges 0
+and 1), a starting position up to 2^31, rotation and GroupNorm on or off, the
+output dtype and an incoming state.  Checked: the bf16 MFMA forms (chunkwise
+output and final state against the recurrent oracle, parallel against the
+parallel oracle), the fp32 vector path, decode steps, the chunkwise backward
+and the gated layer, each at its bar."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +13,7 @@ import torch
 import oracle
 import retentive_network_scale_amd as rn
 from tests import _tol
-from workloads import randn, rotation_theta
+from workloads import multiscale_gamma, randn, rotation_theta
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -65,3 +66,152 @@ def test_random_case(seed):
     op = rn.retention_parallel(qd, kd, vd, g, th, pos0=pos0, gn_eps=eps, out_dtype=c["odt"])
     torch.cuda.synchronize()
     _tol.assert_bf16(op, ref_p, what="parallel " + what)
+
+
+def _gammas(r, H):
+    return torch.tensor([GAMMAS[int(i)] for i in r.integers(len(GAMMAS), size=H)], dtype=torch.float32)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_fp32_vector_path(seed):
+    """fp32 inputs (vector kernels): any even head sizes, fp32 bar."""
+    r = np.random.default_rng(5000 + seed)
+    dk, dv = 2 * int(r.integers(1, 49)), 4 * int(r.integers(1, 33))
+    B, H, L = int(r.integers(1, 3)), int(r.integers(1, 4)), int(r.integers(1, 200))
+    chunk, g, pos0 = int(r.integers(1, 130)), _gammas(r, H), int(r.integers(0, 2 ** 31))
+    th = rotation_theta(dk) if r.integers(2) else None
+    eps = 1e-5 if r.integers(2) else None
+    s0 = randn((B, H, dk, dv), 5100 + seed, 0.5) if r.integers(2) else None
+    q, k = randn((B, H, L, dk), 5200 + seed, dk ** -0.5), randn((B, H, L, dk), 5300 + seed, dk ** -0.5)
+    v = randn((B, H, L, dv), 5400 + seed)
+    what = f"seed {seed}: dk={dk} dv={dv} B={B} H={H} L={L} chunk={chunk} g={g.tolist()} rot={th is not None} gn={eps}"
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    ref_o, ref_s = oracle.recurrent(q, k, v, g, th, pos0=pos0, s_in=s0)
+    o, st = rn.retention_chunkwise(qd, kd, vd, g, chunk, th, pos0=pos0,
+                                   state_in=None if s0 is None else s0.to(DEV), state_out=True, gn_eps=eps)
+    torch.cuda.synchronize()
+    _tol.assert_fp32(o, oracle.groupnorm(ref_o, eps) if eps is not None else ref_o, what="chunkwise " + what)
+    _tol.assert_fp32(st, ref_s, what="final state " + what)
+    ref_p = oracle.parallel(q, k, v, g, th, pos0=pos0)
+    op = rn.retention_parallel(qd, kd, vd, g, th, pos0=pos0, gn_eps=eps)
+    torch.cuda.synchronize()
+    _tol.assert_fp32(op, oracle.groupnorm(ref_p, eps) if eps is not None else ref_p, what="parallel " + what)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_decode_steps(seed):
+    """Decode steps from a random state, every sequence at its own position (up
+    to 2^31), fp32 or bf16 inputs, bf16 or fp32 outputs."""
+    r = np.random.default_rng(6000 + seed)
+    dk, dv = [(16, 24), (64, 128), (128, 256), (256, 512)][int(r.integers(4))]
+    B, H, T = int(r.integers(1, 5)), int(r.integers(1, 4)), int(r.integers(1, 6))
+    g = _gammas(r, H)
+    th = rotation_theta(dk) if r.integers(2) else None
+    eps = 1e-5 if r.integers(2) else None
+    dt = torch.bfloat16 if r.integers(2) else torch.float32
+    odt = torch.bfloat16 if r.integers(2) else torch.float32
+    starts = [int(x) for x in r.integers(0, 2 ** 31 - T, size=B)]
+    q = randn((B, H, T, dk), 6100 + seed, dk ** -0.5, dt)
+    k = randn((B, H, T, dk), 6200 + seed, dk ** -0.5, dt)
+    v = randn((B, H, T, dv), 6300 + seed, 1.0, dt)
+    s0 = randn((B, H, dk, dv), 6400 + seed, 0.5)
+    state = s0.to(DEV)
+    outs = []
+    for t in range(T):
+        pos = torch.tensor([s + t for s in starts], dtype=torch.int32, device=DEV)
+        outs.append(rn.retention_recurrent_step(q[:, :, t].contiguous().to(DEV), k[:, :, t].contiguous().to(DEV),
+                                                v[:, :, t].contiguous().to(DEV), state, pos, g, th, gn_eps=eps,
+                                                out_dtype=odt).clone())
+    o = torch.stack(outs, 2)
+    torch.cuda.synchronize()
+    what = f"seed {seed}: dk={dk} dv={dv} B={B} H={H} T={T} g={g.tolist()} rot={th is not None} gn={eps} {dt} {odt}"
+    for b in range(B):
+        ref_o, ref_s = oracle.recurrent(q[b:b + 1], k[b:b + 1], v[b:b + 1], g, th, pos0=starts[b], s_in=s0[b:b + 1])
+        if eps is not None:
+            ref_o = oracle.groupnorm(ref_o, eps)
+        if odt == torch.float32:
+            _tol.assert_fp32(o[b:b + 1], ref_o, what=f"decode b={b} " + what)
+        else:
+            _tol.assert_bf16(o[b:b + 1], ref_o, what=f"decode b={b} " + what)
+        _tol.assert_fp32(state[b:b + 1], ref_s, what=f"state b={b} " + what)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_backward(seed):
+    """Gradients of chunkwise retention with bf16 inputs (MFMA kernels), fp32 out."""
+    r = np.random.default_rng(7000 + seed)
+    dk, dv = [(64, 128), (128, 128), (128, 256)][int(r.integers(3))]
+    B, H, L = 1, int(r.integers(1, 4)), int(r.integers(1, 300))
+    chunk, g, pos0 = int(r.integers(16, 300)), _gammas(r, H), int(r.integers(0, 2 ** 31))
+    th = rotation_theta(dk) if r.integers(2) else None
+    q = randn((B, H, L, dk), 7100 + seed, dk ** -0.5, torch.bfloat16)
+    k = randn((B, H, L, dk), 7200 + seed, dk ** -0.5, torch.bfloat16)
+    v = randn((B, H, L, dv), 7300 + seed, 1.0, torch.bfloat16)
+    do = randn((B, H, L, dv), 7400 + seed, 1.0, torch.bfloat16)
+    got = rn.retention_chunkwise_bwd(*(t.to(DEV) for t in (q, k, v, do)), g, chunk, th, pos0=pos0,
+                                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.backward(q, k, v, do, g, th, pos0)
+    what = f"seed {seed}: dk={dk} dv={dv} H={H} L={L} chunk={chunk} g={g.tolist()} rot={th is not None}"
+    for name, a, b in zip("qkv", got, ref):
+        _tol.assert_bf16(a, b, slice_dims=2, what=f"d{name} " + what)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_msr_layer(seed):
+    """The gated layer at small random shapes against the oracle layer."""
+    r = np.random.default_rng(8000 + seed)
+    dk, dv = [(64, 128), (128, 256), (256, 512)][int(r.integers(3))]
+    H = int(r.integers(1, 3))
+    dm = 128 * int(r.integers(1, 5))
+    if (H * dk) % 128:
+        H = 2
+    B, L = int(r.integers(1, 3)), int(r.integers(1, 300))
+    chunk, pos0 = int(r.integers(16, 300)), int(r.integers(0, 2 ** 31))
+    g = multiscale_gamma(H)
+    th = rotation_theta(dk)
+    x = randn((B, L, dm), 8100 + seed, 1.0, torch.bfloat16)
+    w = [randn((H * dk, dm), 8200 + seed, 0.05, torch.bfloat16), randn((H * dk, dm), 8300 + seed, 0.05, torch.bfloat16),
+         randn((H * dv, dm), 8400 + seed, 0.05, torch.bfloat16), randn((H * dv, dm), 8500 + seed, 0.05, torch.bfloat16),
+         randn((dm, H * dv), 8600 + seed, 0.05, torch.bfloat16)]
+    y = rn.msr_layer_fwd(x.to(DEV), *(t.to(DEV) for t in w), H, dk, dv, chunk, g, th, pos0=pos0, gn_eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.msr_layer(x, *w, H, dk, dv, g, th, pos0=pos0, gn_eps=1e-5)
+    _tol.assert_bf16(y, ref, slice_dims=0, what=f"msr seed {seed}: dk={dk} dv={dv} H={H} dm={dm} B={B} L={L} chunk={chunk}")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 256)])
+def test_backward_fast_decay_rotated(dk, dv):
+    """gamma = 0 and 0.5 with rotation: every gradient row sums one or a few terms,
+    so the rounding of the rotated operands does not average out."""
+    B, H, L, chunk = 1, 2, 300, 128
+    g = torch.tensor([0.0, 0.5], dtype=torch.float32)
+    th = rotation_theta(dk)
+    q = randn((B, H, L, dk), 7500, dk ** -0.5, torch.bfloat16)
+    k = randn((B, H, L, dk), 7501, dk ** -0.5, torch.bfloat16)
+    v = randn((B, H, L, dv), 7502, 1.0, torch.bfloat16)
+    do = randn((B, H, L, dv), 7503, 1.0, torch.bfloat16)
+    got = rn.retention_chunkwise_bwd(*(t.to(DEV) for t in (q, k, v, do)), g, chunk, th, pos0=12345,
+                                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.backward(q, k, v, do, g, th, 12345)
+    for name, a, b in zip("qkv", got, ref):
+        _tol.assert_bf16(a, b, slice_dims=2, what=f"d{name} dk={dk} dv={dv}")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 256), (256, 512)])
+def test_forward_fast_decay_rotated(dk, dv):
+    """The forward forms at gamma = 0 and 0.5 with rotation (hi+lo scores)."""
+    B, H, L = 1, 2, 300
+    g = torch.tensor([0.0, 0.5], dtype=torch.float32)
+    th = rotation_theta(dk)
+    q = randn((B, H, L, dk), 7600, dk ** -0.5, torch.bfloat16)
+    k = randn((B, H, L, dk), 7601, dk ** -0.5, torch.bfloat16)
+    v = randn((B, H, L, dv), 7602, 1.0, torch.bfloat16)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    ref = oracle.parallel(q, k, v, g, th, pos0=99)
+    o, _ = rn.retention_chunkwise(qd, kd, vd, g, 128, th, pos0=99, out_dtype=torch.float32)
+    op = rn.retention_parallel(qd, kd, vd, g, th, pos0=99, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _tol.assert_bf16(o, ref, what=f"chunkwise dk={dk} dv={dv}")
+    _tol.assert_bf16(op, ref, what=f"parallel dk={dk} dv={dv}")
