@@ -15,7 +15,7 @@ import torch
 import oracle
 import retentive_network_scale_amd as rn
 from tests import _tol
-from workloads import CHUNKWISE_32K, DECODE, PARALLEL_2K, multiscale_gamma, rotation_theta
+from workloads import CHUNKWISE_32K, DECODE, PARALLEL_2K, multiscale_gamma, randn, rotation_theta
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -59,6 +59,33 @@ def test_chunkwise_32k_sampled_rows_and_state():
     rel = np.linalg.norm(sgot - sref) / np.linalg.norm(sref)
     assert rel <= _tol.BF16_REL_L2, f"final state entries rel-L2 {rel:.3e}"
     assert torch.isfinite(o.float()).all()
+
+
+def test_chunkwise_million_tokens_sampled():
+    """One head of 2^20 + 37 tokens (a ragged last chunk), far beyond the
+    workloads: 32-bit offsets, the segment bookkeeping and the scan over 241
+    segments of 17 chunks.  Sampled rows (the first, around 2^19 and 2^20, the
+    last) and final-state entries against the oracle's defining sums."""
+    L, dk, dv, chunk, pos0 = (1 << 20) + 37, 128, 256, 256, 5
+    g = torch.tensor([0.999], dtype=torch.float32)  # slow decay: about 1000 tokens of memory
+    th = rotation_theta(dk)
+    q = randn((1, 1, L, dk), 9100, dk ** -0.5, torch.bfloat16)
+    k = randn((1, 1, L, dk), 9101, dk ** -0.5, torch.bfloat16)
+    v = randn((1, 1, L, dv), 9102, 1.0, torch.bfloat16)
+    o, s = rn.retention_chunkwise(q.to(DEV), k.to(DEV), v.to(DEV), g, chunk, th, pos0=pos0, state_out=True)
+    torch.cuda.synchronize()
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    idx = [(0, 0, 0), (0, 0, (1 << 19) - 1), (0, 0, 1 << 19), (0, 0, (1 << 20) - 1), (0, 0, 1 << 20), (0, 0, L - 1)]
+    rng = np.random.default_rng(11)
+    idx += [(0, 0, int(rng.integers(L))) for _ in range(4)]
+    ref = oracle.rows(qn, kn, vn, g, idx, th, pos0=pos0)
+    got = np.stack([o[b, h, n].float().cpu().numpy() for b, h, n in idx])
+    _tol.assert_bf16(got, ref, slice_dims=1, what="million-token sampled rows")
+    sidx = [(0, 0, int(rng.integers(dk)), int(rng.integers(dv))) for _ in range(8)]
+    sref = oracle.state_entries(kn, vn, g, sidx, th, pos0=pos0)
+    sgot = np.array([s[b, h, a, c].item() for b, h, a, c in sidx])
+    rel = np.linalg.norm(sgot - sref) / np.linalg.norm(sref)
+    assert rel <= _tol.BF16_REL_L2, f"final state entries rel-L2 {rel:.3e}"
 
 
 @pytest.mark.parametrize("chunk", [64, 128, 512, 1024, 2048])
