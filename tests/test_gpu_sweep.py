@@ -215,3 +215,57 @@ def test_forward_fast_decay_rotated(dk, dv):
     torch.cuda.synchronize()
     _tol.assert_bf16(o, ref, what=f"chunkwise dk={dk} dv={dv}")
     _tol.assert_bf16(op, ref, what=f"parallel dk={dk} dv={dv}")
+
+
+def test_max_heads_forms_and_step():
+    """128 heads (the most the interface takes), each with its own decay, through
+    the MFMA forms (chunkwise with GroupNorm, parallel) and one decode step."""
+    B, H, L, dk, dv = 1, 128, 70, 64, 128
+    g = torch.tensor([1.0 - 2.0 ** (-1.0 - h / 16.0) for h in range(H)], dtype=torch.float32)
+    th = rotation_theta(dk)
+    q = randn((B, H, L, dk), 9200, dk ** -0.5, torch.bfloat16)
+    k = randn((B, H, L, dk), 9201, dk ** -0.5, torch.bfloat16)
+    v = randn((B, H, L, dv), 9202, 1.0, torch.bfloat16)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    ref_o, ref_s = oracle.recurrent(q, k, v, g, th, pos0=3)
+    o, s = rn.retention_chunkwise(qd, kd, vd, g, 64, th, pos0=3, state_out=True, gn_eps=1e-5,
+                                  out_dtype=torch.float32)
+    op = rn.retention_parallel(qd, kd, vd, g, th, pos0=3, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _tol.assert_bf16(o, oracle.groupnorm(ref_o, 1e-5), what="chunkwise, 128 heads")
+    _tol.assert_bf16(s, ref_s, what="final state, 128 heads")
+    _tol.assert_bf16(op, ref_o, what="parallel, 128 heads")
+    # one decode step on top of the final state, at position 3 + L
+    q1 = randn((B, H, dk), 9203, dk ** -0.5, torch.bfloat16)
+    k1 = randn((B, H, dk), 9204, dk ** -0.5, torch.bfloat16)
+    v1 = randn((B, H, dv), 9205, 1.0, torch.bfloat16)
+    pos = torch.tensor([3 + L], dtype=torch.int32, device=DEV)
+    st = s.clone()
+    o1 = rn.retention_recurrent_step(q1.to(DEV), k1.to(DEV), v1.to(DEV), st, pos, g, th, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref1, ref_s1 = oracle.recurrent(q1[:, :, None], k1[:, :, None], v1[:, :, None], g, th, pos0=3 + L,
+                                    s_in=s.cpu())
+    _tol.assert_fp32(o1, ref1[:, :, 0], what="decode step, 128 heads")
+    _tol.assert_fp32(st, ref_s1, what="state after the step, 128 heads")
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 129])
+@pytest.mark.parametrize("dk,dv", [(128, 256), (256, 512)])
+def test_tile_edge_lengths(L, dk, dv):
+    """Lengths at and around the 64-token tile, both MFMA forms, with GroupNorm
+    and rotation (hi+lo first blocks) and without."""
+    B, H = 2, 2
+    g = multiscale_gamma(H)
+    th = rotation_theta(dk)
+    q = randn((B, H, L, dk), 9300 + L, dk ** -0.5, torch.bfloat16)
+    k = randn((B, H, L, dk), 9301 + L, dk ** -0.5, torch.bfloat16)
+    v = randn((B, H, L, dv), 9302 + L, 1.0, torch.bfloat16)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    ref = oracle.parallel(q, k, v, g, th, pos0=0)
+    for eps in (None, 1e-5):
+        r = oracle.groupnorm(ref, eps) if eps is not None else ref
+        o, _ = rn.retention_chunkwise(qd, kd, vd, g, 64, th, gn_eps=eps, out_dtype=torch.float32)
+        op = rn.retention_parallel(qd, kd, vd, g, th, gn_eps=eps, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _tol.assert_bf16(o, r, what=f"chunkwise L={L} gn={eps}")
+        _tol.assert_bf16(op, r, what=f"parallel L={L} gn={eps}")
