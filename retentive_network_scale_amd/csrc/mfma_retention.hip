@@ -831,13 +831,21 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   __syncthreads();
   qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, step_s, Qs, LDQ, KsL, nullptr, false, 0.f, 0);
   __syncthreads();
-  const int qblk = w & 3, kh = w >> 2;  // score split: 16 queries x 32 keys per wave
-  u32x4 qreg[KS], qlo[SPLIT ? KS : 1];
+  // score split of the 64 x 64 block over the 8 waves: QW 16-query blocks x KW
+  // 16-key blocks per wave.  Plain scores: 32 queries x 16 keys, each key
+  // operand read from LDS feeding two MFMAs.  hi+lo scores hold twice the query
+  // operands, so there 16 queries x 32 keys.
+  constexpr int QW = SPLIT ? 1 : 2, KW = 2 / QW;
+  const int qp = w % (4 / QW), kq = w / (4 / QW);
+  const int qrow0 = 16 * QW * qp, krow0 = 16 * KW * kq;
+  u32x4 qreg[QW][KS], qlo[QW][SPLIT ? KS : 1];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qreg[ks] = ld_op(Qs + (16 * qblk + l16) * LDQ, 32 * ks, g);
-    if constexpr (SPLIT) qlo[ks] = ld_op(KsL + (16 * qblk + l16) * LDQ, 32 * ks, g);
-  }
+  for (int qq = 0; qq < QW; ++qq)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qreg[qq][ks] = ld_op(Qs + (qrow0 + 16 * qq + l16) * LDQ, 32 * ks, g);
+      if constexpr (SPLIT) qlo[qq][ks] = ld_op(KsL + (qrow0 + 16 * qq + l16) * LDQ, 32 * ks, g);
+    }
   // O^T accumulators: ot[rb][qb4][i] = O^T[w*RW+16rb+4g+i][16qb4+l16]
   f32x4 ot[RB][4];
 #pragma unroll
@@ -883,25 +891,36 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
     v_dma<DV>(Vb, v + (long long)k0 * a.v_sn, a.v_sn, min(BT, c0 + Cc - k0));
     kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, step_s, Ks, LDQ, KsL, nullptr, false, 0.f, 0);
     lds_barrier();  // the keys; the V tile stays in flight
-    // scores S^T[key][query] for keys 32kh..+32, queries 16qblk..+16; decay, mask, -> Ps
+    // scores S^T[key][query] for the wave's keys and queries; decay, mask, -> Ps
 #pragma unroll
-    for (int kb16 = 0; kb16 < 2; ++kb16) {
-      f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = 0; kb < KW; ++kb) {
+      f32x4 sc[QW];
+#pragma unroll
+      for (int qq = 0; qq < QW; ++qq) sc[qq] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 ak = ld_op(Ks + (32 * kh + 16 * kb16 + l16) * LDQ, 32 * ks, g);
-        sc = mfma(ak, qreg[ks], sc);
-        if constexpr (SPLIT) {
-          sc = mfma(ld_op(KsL + (32 * kh + 16 * kb16 + l16) * LDQ, 32 * ks, g), qreg[ks], sc);
-          sc = mfma(ak, qlo[ks], sc);
+        const u32x4 ak = ld_op(Ks + (krow0 + 16 * kb + l16) * LDQ, 32 * ks, g);
+        u32x4 akl;
+        if constexpr (SPLIT) akl = ld_op(KsL + (krow0 + 16 * kb + l16) * LDQ, 32 * ks, g);
+#pragma unroll
+        for (int qq = 0; qq < QW; ++qq) {
+          sc[qq] = mfma(ak, qreg[qq][ks], sc[qq]);
+          if constexpr (SPLIT) {
+            sc[qq] = mfma(akl, qreg[qq][ks], sc[qq]);
+            sc[qq] = mfma(ak, qlo[qq][ks], sc[qq]);
+          }
         }
       }
       // decay and causal mask from the table (delta = qb - kb blocks apart)
-      const int dp = (16 * qblk + l16) - (32 * kh + 16 * kb16 + 4 * g) + (delta ? 128 : 64);
-      float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = sc[i] * (gdel * dt[dp - i]);
-      *(u32x2 *)(Ps + (16 * qblk + l16) * LDT + 32 * kh + 16 * kb16 + 4 * g) = pack4(p[0], p[1], p[2], p[3]);
+      for (int qq = 0; qq < QW; ++qq) {
+        const int qr = qrow0 + 16 * qq + l16, kc = krow0 + 16 * kb + 4 * g;
+        const int dp = qr - kc + (delta ? 128 : 64);
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = sc[qq][i] * (gdel * dt[dp - i]);
+        *(u32x2 *)(Ps + qr * LDT + kc) = pack4(p[0], p[1], p[2], p[3]);
+      }
     }
     wait_vmem();  // this wave's part of the V tile has landed; the barrier publishes all of it
     __syncthreads();
