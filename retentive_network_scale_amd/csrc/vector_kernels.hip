@@ -189,14 +189,59 @@ __global__ __launch_bounds__(VT) void vec_chunkwise_kernel(RetArgs a, float *sta
   }
 }
 
+// Rows r, r + nrg, ... of one thread's VEC state columns in chunks of U rows
+// (all U loads issued before the first update): s <- g s + k_r v, o += q_r s.
+// Advances r past the last whole chunk.
+template <int U, int VEC>
+__device__ __forceinline__ void step_rows(float *S, int &r, int nrg, int dk, int dv, const float *qk, float g,
+                                          const float (&vv)[VEC], float (&oo)[VEC]) {
+  for (; r + (U - 1) * nrg < dk; r += U * nrg) {
+    float s[U][VEC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float *src = S + (long long)(r + u * nrg) * dv;
+      if constexpr (VEC == 4) {
+        const float4 x = *(const float4 *)src;
+        s[u][0] = x.x;
+        s[u][1] = x.y;
+        s[u][2] = x.z;
+        s[u][3] = x.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[u][e] = src[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float kr = qk[RETENTION_MAX_DK + r + u * nrg], qr = qk[r + u * nrg];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        s[u][e] = g * s[u][e] + kr * vv[e];
+        oo[e] += qr * s[u][e];
+      }
+      float *dst = S + (long long)(r + u * nrg) * dv;
+      if constexpr (VEC == 4) {
+        *(float4 *)dst = make_float4(s[u][0], s[u][1], s[u][2], s[u][3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dst[e] = s[u][e];
+      }
+    }
+  }
+}
+
 // One recurrent step per (b, h).  Threads tile the state as (row group, column
 // group of VEC); every thread streams dk / row_groups rows of its columns:
 //   s <- gamma s + k_r v ;  o += q_r s.
 // The state is read and written exactly once, with VEC*4-byte accesses.
 template <int VEC>
 __global__ __launch_bounds__(VT) void vec_step_kernel(RetArgs a, float *state, const int *pos) {
-  __shared__ float qk[2 * RETENTION_MAX_DK];
-  __shared__ float opart[RETENTION_MAX_DV * 4];
+  // The rotated q and k are read only in the state loop and the partial
+  // outputs written only after it (past a barrier): one buffer holds both, so
+  // eight workgroups fit a CU's LDS and a step's workgroups all run at once.
+  static_assert(2 * RETENTION_MAX_DK <= RETENTION_MAX_DV * 4, "q, k fit the partial-output buffer");
+  __shared__ float qk_opart[RETENTION_MAX_DV * 4];
+  float *const qk = qk_opart, *const opart = qk_opart;
   __shared__ float red[VT / 64];
   const int t = threadIdx.x;
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
@@ -235,48 +280,13 @@ __global__ __launch_bounds__(VT) void vec_step_kernel(RetArgs a, float *state, c
   }
   if (active) {
     float *S = state + (long long)bh * a.dk * a.dv + cg * VEC;
-    constexpr int U = 8;
+    // rows r, r + nrg, ...: chunks of 16 rows (all of them in flight), then 8,
+    // then one at a time.  At 16 the registers allow three waves per SIMD,
+    // which streams faster than more waves with fewer loads each.
     int r = rg;
-    for (; r + (U - 1) * nrg < a.dk; r += U * nrg) {
-      float s[U][VEC];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float *src = S + (long long)(r + u * nrg) * a.dv;
-        if constexpr (VEC == 4) {
-          float4 x = *(const float4 *)src;
-          s[u][0] = x.x; s[u][1] = x.y; s[u][2] = x.z; s[u][3] = x.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) s[u][e] = src[e];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float kr = qk[RETENTION_MAX_DK + r + u * nrg], qr = qk[r + u * nrg];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          s[u][e] = g * s[u][e] + kr * vv[e];
-          oo[e] += qr * s[u][e];
-        }
-        float *dst = S + (long long)(r + u * nrg) * a.dv;
-        if constexpr (VEC == 4) {
-          *(float4 *)dst = make_float4(s[u][0], s[u][1], s[u][2], s[u][3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) dst[e] = s[u][e];
-        }
-      }
-    }
-    for (; r < a.dk; r += nrg) {
-      float *row = S + (long long)r * a.dv;
-      const float kr = qk[RETENTION_MAX_DK + r], qr = qk[r];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        float x = g * row[e] + kr * vv[e];
-        row[e] = x;
-        oo[e] += qr * x;
-      }
-    }
+    step_rows<16, VEC>(S, r, nrg, a.dk, a.dv, qk, g, vv, oo);
+    step_rows<8, VEC>(S, r, nrg, a.dk, a.dv, qk, g, vv, oo);
+    step_rows<1, VEC>(S, r, nrg, a.dk, a.dv, qk, g, vv, oo);
   }
   // reduce the row groups' partial outputs through LDS, up to 4 groups per pass
   for (int base = 0; base < nrg; base += 4) {
