@@ -334,6 +334,60 @@ def pmc_summary(name, fetch_csv, write_csv, command, out_dir=None):
     print(open(out).read())
 
 
+# MI355X layout the utilisation counters are normalised by: SQ counters are summed
+# over all CUs (and SIMDs), GRBM_GUI_ACTIVE over the XCDs.
+N_XCD, N_CU, SIMD_PER_CU = 8, 256, 4
+UTIL_COUNTERS = ("SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_WAVE_CYCLES SQ_WAIT_INST_LDS SQ_INSTS_LDS_LOAD_BANDWIDTH "
+                 "SQ_INSTS_LDS_STORE_BANDWIDTH SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
+
+
+def util_summary(name, counters_csv, command, out_dir=None):
+    """Turns one rocprofv3 --pmc counter_collection.csv (the UTIL_COUNTERS set) of a
+    `bench.py --only ...` run into profiles/util_<name>.txt: per kernel, the
+    dispatch-averaged counters and the fractions derived from them.
+      active cycles per XCD = GRBM_GUI_ACTIVE / N_XCD
+      MFMA busy  = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * N_CU * SIMD_PER_CU)
+      LDS busy   = SQ_LDS_IDX_ACTIVE / (cycles * N_CU)
+      bank conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+      LDS wait   = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES"""
+    import csv
+    import collections
+    sums = collections.defaultdict(lambda: collections.defaultdict(float))
+    counts = collections.defaultdict(lambda: collections.defaultdict(int))
+    for r in csv.DictReader(open(counters_csv)):
+        k = r["Kernel_Name"]
+        if not k.startswith(("ret::", "void ret::")):
+            continue
+        sums[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        counts[k][r["Counter_Name"]] += 1
+    if not sums:
+        raise SystemExit(f"{counters_csv}: no kernels of this library")
+    out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"util_{name}.txt")
+    with open(out, "w") as fh:
+        fh.write(f"# MFMA and LDS utilisation of the {name} kernels: rocprofv3 PMC counters, averaged per dispatch.\n"
+                 f"# Normalised for {N_XCD} XCDs, {N_CU} CUs, {SIMD_PER_CU} SIMDs per CU:\n"
+                 "#   cycles = GRBM_GUI_ACTIVE / XCDs; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * SIMDs);\n"
+                 "#   lds_busy = SQ_LDS_IDX_ACTIVE / (cycles * CUs); lds_bank_conflict = SQ_LDS_BANK_CONFLICT /\n"
+                 "#   SQ_LDS_IDX_ACTIVE; lds_wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES\n")
+        for c in command:
+            fh.write(f"# command: {c}\n")
+        for k in sorted(sums, key=lambda k: -sums[k].get("GRBM_GUI_ACTIVE", 0.0)):
+            avg = {c: sums[k][c] / counts[k][c] for c in sums[k]}
+            cyc = avg.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+            if cyc <= 0:
+                continue
+            mfma = avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * N_CU * SIMD_PER_CU)
+            lds = avg.get("SQ_LDS_IDX_ACTIVE", 0.0) / (cyc * N_CU)
+            conf = avg.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(avg.get("SQ_LDS_IDX_ACTIVE", 0.0), 1.0)
+            wait = avg.get("SQ_WAIT_INST_LDS", 0.0) / max(avg.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+            n = max(counts[k].values())
+            fh.write(f"\nkernel = {k[:110]}\ndispatches = {n}\ncycles_per_xcd = {cyc:.0f}\n"
+                     f"mfma_busy = {mfma:.3f}\nlds_busy = {lds:.3f}\nlds_bank_conflict = {conf:.3f}\n"
+                     f"lds_wait = {wait:.3f}\n")
+        fh.write(f"\nsrc_sha = {_src_sha()}\n")
+    print(open(out).read())
+
+
 def stats_summary(trace_dir, command):
     """Markdown tables of a rocprofv3 --kernel-trace --stats run: the kernel_stats.csv
     as written, then the kernel_trace.csv grouped by kernel and grid size (one
@@ -489,6 +543,8 @@ def main():
     ap.add_argument("--pmc-summary", nargs=3, metavar=("NAME", "FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_NAME.txt from two rocprofv3 PMC runs (no GPU needed)")
     ap.add_argument("--pmc-command", action="append", default=[], help="command line recorded in the summary")
+    ap.add_argument("--util-summary", nargs=2, metavar=("NAME", "COUNTERS_CSV"),
+                    help="write profiles/util_NAME.txt from one rocprofv3 PMC run of UTIL_COUNTERS (no GPU needed)")
     ap.add_argument("--stats-summary", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
                     help="print a rocprofv3 --kernel-trace --stats output folder as tables (no GPU needed)")
     args = ap.parse_args()
@@ -497,6 +553,9 @@ def main():
         return
     if args.stats_summary:
         stats_summary(*args.stats_summary)
+        return
+    if args.util_summary:
+        util_summary(*args.util_summary, args.pmc_command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

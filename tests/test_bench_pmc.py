@@ -63,3 +63,37 @@ def test_chunkwise_three_kernels_per_call(tmp_path):
     vals = _summary(tmp_path, "chunkwise_32k", fetch, write)
     assert float(vals["fetch_kib_per_call"]) == 420.0
     assert float(vals["write_kib_per_call"]) == 190.0
+
+
+def test_util_summary_normalisation(tmp_path):
+    """bench.util_summary: per-dispatch averages of the utilisation counters and
+    the fractions derived from them (cycles per XCD, MFMA busy per SIMD cycle,
+    LDS busy per CU cycle, conflict and wait ratios); kernels of other libraries
+    are left out."""
+    k = "void ret::qblock_kernel<256, 512, true, false>(ret::RetArgs, ret::TaskGeom, unsigned short const*)"
+    cyc = 1000.0  # active cycles per XCD in each dispatch
+    simds = bench.N_CU * bench.SIMD_PER_CU
+    per_dispatch = {"GRBM_GUI_ACTIVE": cyc * bench.N_XCD, "SQ_VALU_MFMA_BUSY_CYCLES": 0.25 * cyc * simds,
+                    "SQ_LDS_IDX_ACTIVE": 0.5 * cyc * bench.N_CU, "SQ_LDS_BANK_CONFLICT": 0.1 * 0.5 * cyc * bench.N_CU,
+                    "SQ_WAIT_INST_LDS": 30.0, "SQ_WAVE_CYCLES": 300.0}
+    path = tmp_path / "c.csv"
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(COLS)
+        for d in range(2):  # two dispatches: the second reads twice the first, averaging to 1.5x
+            for c, v in per_dispatch.items():
+                w.writerow([d, k, c, v * (1 + d) / 1.5])
+                w.writerow([d, "at::native::other_kernel", c, 7.0])
+    bench.util_summary("t", str(path), ["cmd"], out_dir=str(tmp_path))
+    vals = {}
+    for line in open(os.path.join(tmp_path, "util_t.txt")):
+        if "=" in line and not line.startswith("#"):
+            key, v = line.split("=", 1)
+            vals[key.strip()] = v.strip()
+    assert vals["kernel"] == k[:110]
+    assert vals["dispatches"] == "2"
+    assert float(vals["cycles_per_xcd"]) == cyc
+    assert abs(float(vals["mfma_busy"]) - 0.25) < 1e-3
+    assert abs(float(vals["lds_busy"]) - 0.5) < 1e-3
+    assert abs(float(vals["lds_bank_conflict"]) - 0.1) < 1e-3
+    assert abs(float(vals["lds_wait"]) - 0.1) < 1e-3
