@@ -343,7 +343,8 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
   hipError_t e;
   float *dqr = (float *)(ws + p.dq), *dkr = (float *)(ws + p.dk), *dvr = (float *)(ws + p.dv);
   void *cws = ws + p.cws;
-  if (use_mfma(dk, dv, in_dtype) && use_mfma(dv, dk, in_dtype) && (long long)dk * dv <= 128 * 256) {
+  if (use_mfma(dk, dv, in_dtype) && use_mfma(dv, dk, in_dtype) && chunk_state_in_regs(B, H, L, dk, dv, chunk) &&
+      chunk_state_in_regs(B, H, L, dv, dk, chunk)) {
     // the MFMA kernels read the reversed sequences themselves: only the rotated
     // keys and queries are prepared (forward order; the p.kr and p.qrev slots)
     void *kr = ws + p.kr, *qr = ws + p.qrev;

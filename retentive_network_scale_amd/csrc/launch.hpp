@@ -33,8 +33,12 @@ struct ChunkPlan {
   size_t seg_bytes;   // fp32 segment states [B*H][nseg][dk][dv]
   size_t sinT_bytes;  // bf16 incoming segment states, transposed [B*H][nseg][dv][dk]
   size_t ws_bytes;    // total
+  bool in_regs;       // design A (segment-output kernel); else design B (query-block kernel per chunk)
 };
 ChunkPlan chunk_plan(int B, int H, int L, int dk, int dv, int chunk);
+// Whether chunkwise retention of these dimensions runs design A, the only one
+// that reads reversed inputs (RetArgs::in_rev).
+bool chunk_state_in_regs(int B, int H, int L, int dk, int dv, int chunk);
 hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &plan, void *ws,
                                  const float *state_in, float *state_out, hipStream_t st);
 

@@ -1456,17 +1456,32 @@ static int state_dvw(int dk, int dv) {
   return dvw;
 }
 
+// Segments the segment-state pass aims for: about one workgroup per CU.
+constexpr int SEG_TARGET = 256;
+
+// Design A (the segment-output kernel, the state in its accumulators through a
+// segment) when the state fits and either the chunk has at most KRES key
+// blocks (its rotated keys stay in LDS) or there are chunks enough for a
+// segment per CU; otherwise design B (the query-block kernel per chunk and
+// 64-query block, with the bf16 state entering every chunk), whose tasks fill
+// the GPU where design A's few long segments cannot (at L = 32768, 8 heads:
+// chunk 2048 639 us against 1136 us; chunks 512 and 1024 stay faster in A).
+// Only design A reads reversed inputs (RetArgs::in_rev).
+bool chunk_state_in_regs(int B, int H, int L, int dk, int dv, int chunk) {
+  if (!state_in_regs(dk, dv)) return false;
+  if (chunk <= KRES * BT) return true;
+  return (long long)B * H * ((L + chunk - 1) / chunk) >= SEG_TARGET;
+}
+
 ChunkPlan chunk_plan(int B, int H, int L, int dk, int dv, int chunk) {
   ChunkPlan p;
   const int nsplit = dv / state_dvw(dk, dv);
   const int nchunks = (L + chunk - 1) / chunk;
   const int units = B * H * nsplit;
-  // states that fit one workgroup's accumulators stay in registers through a
-  // segment; larger ones are handed to the query-block kernel as the bf16 state
-  // entering every chunk, so there every chunk is a segment of its own
-  const bool in_regs = state_in_regs(dk, dv);
-  const int target = 256;  // segment-state pass: about one workgroup per CU
-  int nseg = in_regs ? (target + units - 1) / units : nchunks;
+  // design A: segments of several chunks; design B: every chunk a segment of its own
+  const bool in_regs = chunk_state_in_regs(B, H, L, dk, dv, chunk);
+  p.in_regs = in_regs;
+  int nseg = in_regs ? (SEG_TARGET + units - 1) / units : nchunks;
   if (nseg > nchunks) nseg = nchunks;
   if (nseg < 1) nseg = 1;
   p.seg_chunks = (nchunks + nseg - 1) / nseg;
@@ -1583,16 +1598,18 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
 template <int DK, int DV>
 static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, const float *state_in,
                                 float *state_out, hipStream_t st) {
-  constexpr bool IN_REGS = (long long)DK * DV <= IN_REGS_MAX;
-  constexpr int DVW1 = IN_REGS ? DV : (DK * DV > SPLIT_STATE_MAX ? (int)(SPLIT_STATE_MAX / DK) : DV);
+  constexpr bool FITS = (long long)DK * DV <= IN_REGS_MAX;  // design A possible
+  constexpr int DVW1 = FITS ? DV : (DK * DV > SPLIT_STATE_MAX ? (int)(SPLIT_STATE_MAX / DK) : DV);
+  const bool in_regs = FITS && p.in_regs;
+  if (a.in_rev && !in_regs) return hipErrorNotSupported;  // reversed inputs: design A only
   float *seg = (float *)ws;
-  uint16_t *sinT = IN_REGS ? nullptr : (uint16_t *)(ws + p.seg_bytes);
+  uint16_t *sinT = in_regs ? nullptr : (uint16_t *)(ws + p.seg_bytes);
   TaskGeom geo{p.nseg, p.seg_chunks, DV / DVW1, 1, 0, (a.L + a.chunk - 1) / a.chunk};
   geo.ntasks = a.B * a.H * geo.nseg * geo.nsplit;
   hipLaunchKernelGGL((seg_state_kernel<DK, DVW1>), dim3(xcd_grid(geo.ntasks)), dim3(NT), 0, st, a, geo, seg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (IN_REGS) {
+  if (in_regs) {
     const long long n4 = (long long)a.dk * a.dv / 4;
     hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)((n4 + 255) / 256), a.B * a.H), dim3(256), 0, st, a, geo, seg,
                        state_in, state_out);
@@ -1603,7 +1620,8 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (IN_REGS) {
+  if constexpr (FITS) {
+    if (!in_regs) return run_qblocks<DK, DV>(a, geo, false, sinT, st);
     geo.ntasks = a.B * a.H * geo.nseg;
     const dim3 grid(xcd_grid(geo.ntasks));
     if ((a.use_gn && a.use_theta) || split_all_blocks(a))

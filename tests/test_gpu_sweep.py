@@ -269,3 +269,48 @@ def test_tile_edge_lengths(L, dk, dv):
         torch.cuda.synchronize()
         _tol.assert_bf16(o, r, what=f"chunkwise L={L} gn={eps}")
         _tol.assert_bf16(op, r, what=f"parallel L={L} gn={eps}")
+
+
+@pytest.mark.parametrize("dk,dv,chunk,L,gn", [(128, 256, 512, 1100, False), (128, 256, 1024, 2100, True),
+                                             (64, 128, 2048, 2100, False), (256, 128, 512, 700, True)])
+def test_long_chunks_state_in_registers(dk, dv, chunk, L, gn):
+    """Chunks longer than four 64-token key blocks, too few for a segment per CU
+    (here 2 heads of a short sequence), with states that fit the segment-output
+    kernel run the per-chunk query-block path instead: output (with GroupNorm or
+    not), incoming and final state against the recurrent oracle, at ragged
+    lengths."""
+    B, H = 1, 2
+    g = torch.tensor([0.96875, 0.999], dtype=torch.float32)
+    th = rotation_theta(dk)
+    q = randn((B, H, L, dk), 9400, dk ** -0.5, torch.bfloat16)
+    k = randn((B, H, L, dk), 9401, dk ** -0.5, torch.bfloat16)
+    v = randn((B, H, L, dv), 9402, 1.0, torch.bfloat16)
+    s_in = randn((B, H, dk, dv), 9403, 0.1, torch.float32)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    eps = 1e-5 if gn else None
+    ref_o, ref_s = oracle.recurrent(q, k, v, g, th, pos0=777, s_in=s_in)
+    o, s = rn.retention_chunkwise(qd, kd, vd, g, chunk, th, pos0=777, state_in=s_in.to(DEV), state_out=True,
+                                  gn_eps=eps, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    what = f"dk={dk} dv={dv} chunk={chunk} L={L} gn={gn}"
+    _tol.assert_bf16(o, oracle.groupnorm(ref_o, eps) if gn else ref_o, what="chunkwise " + what)
+    _tol.assert_bf16(s, ref_s, what="final state " + what)
+
+
+def test_backward_long_chunk():
+    """The backward at a chunk longer than four key blocks and too few chunks for
+    a segment per CU: its inner retentions then run the per-chunk path, on
+    explicitly reversed copies (that path reads inputs in order only)."""
+    dk, dv, B, H, L, chunk = 128, 256, 1, 2, 700, 512
+    g = torch.tensor([0.96875, 0.999], dtype=torch.float32)
+    th = rotation_theta(dk)
+    q = randn((B, H, L, dk), 9500, dk ** -0.5, torch.bfloat16)
+    k = randn((B, H, L, dk), 9501, dk ** -0.5, torch.bfloat16)
+    v = randn((B, H, L, dv), 9502, 1.0, torch.bfloat16)
+    do = randn((B, H, L, dv), 9503, 1.0, torch.bfloat16)
+    got = rn.retention_chunkwise_bwd(*(t.to(DEV) for t in (q, k, v, do)), g, chunk, th, pos0=4242,
+                                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.backward(q, k, v, do, g, th, 4242)
+    for name, a, b in zip("qkv", got, ref):
+        _tol.assert_bf16(a, b, slice_dims=2, what=f"d{name} chunk={chunk}")
