@@ -1098,7 +1098,13 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) st[dkb][rb] *= gc;
       }
-      for (int kb = 0; kb <= qb; ++kb) {
+      // key blocks in zigzag order: forward for even query blocks, backward for
+      // odd ones, so the V blocks of one block's last visits are the next
+      // block's first and still in L2 (the sums do not depend on the order)
+      const bool fwd = (qb & 1) == 0;
+      for (int vi = 0; vi <= qb; ++vi) {
+        const int kb = fwd ? vi : qb - vi;
+        const bool last_visit = vi == qb;
         const int k0 = c0 + kb * BT;
         const bool upd = carry && last_qb;
         const int delta = qb - kb;
@@ -1125,22 +1131,23 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
         // at its block boundary: no barrier between these stores and the scores
         if constexpr (!RES) __syncthreads();
         // next visit: next key block of this query block, else the first key block
-        // of the next query block (of this chunk, or of the next chunk).  Its loads
-        // are issued in two parts -- K before the scores, V before PV -- so the
-        // memory system absorbs them while the MFMAs run.
-        int nk0 = k0 + BT, nend = c0 + Cc;
-        if (kb == qb) {
-          nk0 = last_qb ? c0 + Cc : c0;
-          nend = min(a.L, nk0 + a.chunk);
+        // of the next query block (of this chunk, or query block 0 of the next
+        // chunk).  Its loads are issued in two parts -- K before the scores, V
+        // before PV -- so the memory system absorbs them while the MFMAs run.
+        int nk0 = k0 + (fwd ? BT : -BT), nend = c0 + Cc;
+        if (last_visit) {
+          const int nc0 = last_qb ? c0 + Cc : c0, nqb = last_qb ? 0 : qb + 1;
+          nk0 = nc0 + ((nqb & 1) == 0 ? 0 : nqb * BT);
+          nend = min(a.L, nc0 + a.chunk);
         }
         const bool has_next = nk0 < t_hi;
         if constexpr (!RES)
           if (has_next) kio.fetch(tile_src(k, nk0, min(BT, nend - nk0), a.q_sn, a), a.q_sn, min(BT, nend - nk0), a.in_rev);
-        // at the diagonal visit: the next block's query tile (and resident key
+        // at the last visit: the next block's query tile (and resident key
         // tile), committed at the next block boundary.  Issued this late so the
         // registers are free during the earlier visits.
-        if (kb == qb) {
-          const int nq0 = last_qb ? nk0 : q0 + BT;
+        if (last_visit) {
+          const int nq0 = last_qb ? c0 + Cc : q0 + BT;
           if (nq0 < t_hi) {
             qio.fetch(tile_src(q, nq0, min(BT, nend - nq0), a.q_sn, a), a.q_sn, min(BT, nend - nq0), a.in_rev);
             if constexpr (RES)
