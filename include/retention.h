@@ -71,6 +71,10 @@ typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
 #define RETENTION_MAX_HEADS 128
 #define RETENTION_MAX_DK 512
 #define RETENTION_MAX_DV 1024
+#define RETENTION_MAX_TOKEN_HEADS (1LL << 28) /* B * H * L of one call */
+/* Positions: every absolute position is a non-negative int32, pos0 + L <=
+ * RETENTION_POS_LIMIT (INVALID_ARG beyond), as for the decode step's int32 pos. */
+#define RETENTION_POS_LIMIT (1LL << 31)
 
 int retention_abi_version(void);
 const char *retention_status_string(int status);
@@ -102,6 +106,8 @@ ret_status_t retention_parallel(const void *q, const void *k, const void *v, voi
  *   workspace  : device scratch of at least retention_chunkwise_workspace_bytes()
  *                bytes (NULL allowed when that is 0); its contents on entry do
  *                not matter.  Calls sharing a workspace must not overlap.
+ * A chunk longer than L is taken as L (one chunk: the parallel form), here and
+ * in every call and workspace query that takes a chunk size.
  */
 size_t retention_chunkwise_workspace_bytes(int B, int H, int L, int dk, int dv, int chunk,
                                            ret_dtype_t in_dtype);
@@ -167,8 +173,8 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
  *   w_o : [d_model, H*dv] bf16
  * UNSUPPORTED unless d_model, H*dk and H*dv are multiples of 128 and (dk, dv) is
  * one of the MFMA pairs listed under retention_parallel.
- * The four projections and W_O are plain GEMMs run through hipBLASLt (this
- * library's own GEMM kernel where hipBLASLt offers no algorithm).  When w_q,
+ * The four projections and W_O are plain GEMMs run through hipBLASLt; a shape
+ * for which hipBLASLt offers no algorithm returns UNSUPPORTED.  When w_q,
  * w_k, w_v and w_g are stored back to back in that order (one fused
  * [2 H dk + 2 H dv, d_model] matrix), the projections run as one GEMM.  The first
  * call on a device creates that device's hipBLASLt handle, kept until the

@@ -56,6 +56,7 @@ def _load():
         "orc_layernorm": [_D, _l, _l, ctypes.c_double],
         "orc_gelu": [_D, _l],
         "orc_backward": [_D, _D, _D, _D, _l, _l, _l, _l, _l, _D, _D, _ll, _D, _D, _D],
+        "orc_backward_recurrent": [_D, _D, _D, _D, _l, _l, _l, _l, _l, _D, _D, _ll, _D, _D, _D],
         "orc_backward_rows": [_D, _D, _D, _D, _l, _l, _l, _l, _l, _D, _D, _ll, ctypes.c_int, _L, _l, _D],
     }
     for name, args in sigs.items():
@@ -180,6 +181,17 @@ def backward(q, k, v, do, gamma, theta=None, pos0=0):
     dq, dkk, dvv = np.empty((B, H, L, dk)), np.empty((B, H, L, dk)), np.empty((B, H, L, dv))
     _load().orc_backward(_p(q), _p(k), _p(v), _p(do), B, H, L, dk, dv, _p(g), _p(_theta(theta)), pos0,
                          _p(dq), _p(dkk), _p(dvv))
+    return dq, dkk, dvv
+
+
+def backward_recurrent(q, k, v, do, gamma, theta=None, pos0=0):
+    """The same gradients by the adjoint of the recurrent form (O(L dk dv) per
+    (b, h)): a forward sweep of the state for dq, a reverse sweep for dk and dv."""
+    q, k, v, do, g = as_f64(q), as_f64(k), as_f64(v), as_f64(do), as_f64(gamma)
+    B, H, L, dk, dv = _dims(q, v)
+    dq, dkk, dvv = np.empty((B, H, L, dk)), np.empty((B, H, L, dk)), np.empty((B, H, L, dv))
+    _load().orc_backward_recurrent(_p(q), _p(k), _p(v), _p(do), B, H, L, dk, dv, _p(g), _p(_theta(theta)), pos0,
+                                   _p(dq), _p(dkk), _p(dvv))
     return dq, dkk, dvv
 
 

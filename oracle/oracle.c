@@ -320,6 +320,52 @@ void orc_backward(const double *q, const double *k, const double *v, const doubl
   }
 }
 
+/* The same gradients from the recurrent representation (P2 Sec. 2.1 (2)) by
+ * its adjoint, a derivation independent of the double sum above and O(L dk dv)
+ * per (b, h).  The forward state S_n = gamma S_{n-1} + k~_n^T v_n (zero before
+ * token 0) gives o_n = q~_n S_n, so
+ *   dq~_n = S_n dO_n^T                                  (forward sweep)
+ * and the reverse-time state G_n = gamma G_{n+1} + q~_n^T dO_n (zero after the
+ * last token), which gathers the pull of every query at or after n, gives
+ *   dk~_n = G_n v_n^T,   dv_n = k~_n G_n                 (backward sweep)
+ * with dq_n = R_n^T dq~_n and dk_n = R_n^T dk~_n. */
+void orc_backward_recurrent(const double *q, const double *k, const double *v, const double *dO, long B,
+                            long H, long L, long dk, long dv, const double *gamma, const double *theta,
+                            long long pos0, double *dq, double *dkk, double *dvv) {
+#pragma omp parallel for schedule(dynamic)
+  for (long u = 0; u < B * H; ++u) {
+    double g = gamma[u % H];
+    double *S = calloc(dk * dv, sizeof(double));
+    double *xr = malloc(sizeof(double) * dk), *acc = malloc(sizeof(double) * dk);
+    for (long n = 0; n < L; ++n) { /* forward sweep: dq */
+      rotate_row(k + (u * L + n) * dk, dk, pos0 + n, theta, xr);
+      const double *vn = v + (u * L + n) * dv, *don = dO + (u * L + n) * dv;
+      for (long i = 0; i < dk; ++i)
+        for (long j = 0; j < dv; ++j) S[i * dv + j] = g * S[i * dv + j] + xr[i] * vn[j];
+      for (long i = 0; i < dk; ++i) acc[i] = dot(S + i * dv, don, dv);
+      unrotate_row(acc, dk, pos0 + n, theta, dq + (u * L + n) * dk);
+    }
+    double *G = S;
+    for (long i = 0; i < dk * dv; ++i) G[i] = 0.0;
+    for (long n = L - 1; n >= 0; --n) { /* backward sweep: dk, dv */
+      rotate_row(q + (u * L + n) * dk, dk, pos0 + n, theta, xr);
+      const double *vn = v + (u * L + n) * dv, *don = dO + (u * L + n) * dv;
+      for (long i = 0; i < dk; ++i)
+        for (long j = 0; j < dv; ++j) G[i * dv + j] = g * G[i * dv + j] + xr[i] * don[j];
+      for (long i = 0; i < dk; ++i) acc[i] = dot(G + i * dv, vn, dv);
+      unrotate_row(acc, dk, pos0 + n, theta, dkk + (u * L + n) * dk);
+      rotate_row(k + (u * L + n) * dk, dk, pos0 + n, theta, xr);
+      double *dvn = dvv + (u * L + n) * dv;
+      for (long j = 0; j < dv; ++j) dvn[j] = 0.0;
+      for (long i = 0; i < dk; ++i)
+        for (long j = 0; j < dv; ++j) dvn[j] += xr[i] * G[i * dv + j];
+    }
+    free(S);
+    free(xr);
+    free(acc);
+  }
+}
+
 /* Selected rows of the gradients above: which = 0 gives dq row n (a sum over
  * m <= n), 1 gives dk row n and 2 gives dv row n (sums over later tokens).
  * idx holds (b, h, n) triples; out receives dk values per row for which 0 and 1,

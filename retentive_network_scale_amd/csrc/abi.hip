@@ -63,8 +63,10 @@ ret_status_t check_common(int B, int H, int L, int dk, int dv, const float *gamm
   }
   if (isnan(gn_eps) || (gn_eps >= 0.0f && !isfinite(gn_eps)))
     return fail(RET_ERR_INVALID_ARG, "gn_eps must be finite (or negative for no GroupNorm)");
-  if (pos0 < 0 || pos0 > (1LL << 52) - (long long)L)
-    return fail(RET_ERR_INVALID_ARG, "pos0=%lld outside [0, 2^52 - L]", pos0);
+  if ((long long)B * H * L > RETENTION_MAX_TOKEN_HEADS)
+    return fail(RET_ERR_UNSUPPORTED, "B*H*L=%lld above %lld", (long long)B * H * L, RETENTION_MAX_TOKEN_HEADS);
+  if (pos0 < 0 || pos0 > RETENTION_POS_LIMIT - (long long)L)
+    return fail(RET_ERR_INVALID_ARG, "pos0=%lld outside [0, 2^31 - L]", pos0);
   return RET_OK;
 }
 
@@ -244,6 +246,8 @@ ret_status_t retention_parallel(const void *q, const void *k, const void *v, voi
 size_t retention_chunkwise_workspace_bytes(int B, int H, int L, int dk, int dv, int chunk,
                                            ret_dtype_t in_dtype) {
   if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+  if ((long long)B * H * L > RETENTION_MAX_TOKEN_HEADS) return 0;
+  chunk = std::min(chunk, L);
   if (use_mfma(dk, dv, in_dtype)) return chunk_plan(B, H, L, dk, dv, chunk).ws_bytes;
   return vec_chunk_ws(B, H, dk, dv);
 }
@@ -257,6 +261,7 @@ ret_status_t retention_chunkwise(const void *q, const void *k, const void *v, vo
   ret_status_t s = check_common(B, H, L, dk, dv, gamma, theta, pos0, gn_eps, in_dtype, out_dtype);
   if (s != RET_OK) return s;
   if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk=%d must be positive", chunk);
+  chunk = std::min(chunk, std::max(L, 1));
   if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)))
     return fail(RET_ERR_INVALID_ARG, "state pointers must be 16-byte aligned");
   const size_t ns = (size_t)B * H * dk * dv * sizeof(float);
@@ -300,6 +305,8 @@ ret_status_t retention_chunkwise(const void *q, const void *k, const void *v, vo
 
 size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_t in_dtype) {
   if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+  if ((long long)B * H * L > RETENTION_MAX_TOKEN_HEADS) return 0;
+  chunk = std::min(chunk, L);
   return bwd_plan(B, H, L, dk, dv, chunk, in_dtype).total;
 }
 
@@ -311,6 +318,7 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
   ret_status_t s = check_common(B, H, L, dk, dv, gamma, theta, pos0, -1.0f, in_dtype, out_dtype);
   if (s != RET_OK) return s;
   if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk=%d must be positive", chunk);
+  chunk = std::min(chunk, std::max(L, 1));
   if (dk % 8 || dv % 8) return fail(RET_ERR_UNSUPPORTED, "the backward needs dk and dv multiples of 8");
   if (dv > RETENTION_MAX_DK)  // dv is the query/key width of two of the inner retentions
     return fail(RET_ERR_UNSUPPORTED, "the backward needs dv <= %d", RETENTION_MAX_DK);

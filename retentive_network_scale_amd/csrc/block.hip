@@ -1,7 +1,7 @@
 // Row-wise passes of the pre-LN residual block around the gated layer ("Retentive
 // Network" paper summary, block equations: Y = MSR(LN(X)) + X, X' = FFN(LN(Y)) + Y,
 // FFN(X) = gelu(X W_1) W_2).  The residual adds ride in the GEMMs (beta = 1);
-// these kernels are the LayerNorm, the gelu and a fallback add.
+// these kernels are the LayerNorm and the gelu.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -68,20 +68,6 @@ __global__ void gelu_bf16_kernel(uint16_t *x, long long n8) {
   *(uint4 *)(x + 8 * i) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
 }
 
-// c <- c + r, 8 bf16 values per thread (n % 8 == 0).
-__global__ void add_bf16_kernel(uint16_t *c, const uint16_t *r, long long n8) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const uint4 a = *(const uint4 *)(c + 8 * i), b = *(const uint4 *)(r + 8 * i);
-  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    o[e] = pack_bf2(__uint_as_float(aw[e] << 16) + __uint_as_float(bw[e] << 16),
-                    __uint_as_float(aw[e] & 0xffff0000u) + __uint_as_float(bw[e] & 0xffff0000u));
-  *(uint4 *)(c + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 hipError_t launch_layernorm_bf16(const uint16_t *x, uint16_t *y, long long rows, int d, float eps, hipStream_t st) {
   hipLaunchKernelGGL(layernorm_bf16_kernel, dim3((unsigned)rows), dim3(256), 0, st, x, y, d, eps);
   return hipGetLastError();
@@ -90,12 +76,6 @@ hipError_t launch_layernorm_bf16(const uint16_t *x, uint16_t *y, long long rows,
 hipError_t launch_gelu_bf16(uint16_t *x, long long n, hipStream_t st) {
   const long long n8 = n / 8;
   hipLaunchKernelGGL(gelu_bf16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, x, n8);
-  return hipGetLastError();
-}
-
-hipError_t launch_add_bf16(uint16_t *c, const uint16_t *r, long long n, hipStream_t st) {
-  const long long n8 = n / 8;
-  hipLaunchKernelGGL(add_bf16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, c, r, n8);
   return hipGetLastError();
 }
 

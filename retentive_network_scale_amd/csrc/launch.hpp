@@ -42,26 +42,6 @@ bool chunk_state_in_regs(int B, int H, int L, int dk, int dv, int chunk);
 hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &plan, void *ws,
                                  const float *state_in, float *state_out, hipStream_t st);
 
-// bf16 GEMM: C[M][N] = A[M][K] . W^T with W stored [N][K]; see gemm.hip.
-// Requires K % 64 == 0 and every segment's n % 128 == 0.
-enum { GEMM_PLAIN = 0, GEMM_HEADS = 1, GEMM_SWISH = 2 };
-struct GemmSeg {
-  const uint16_t *w;  // [n][K]
-  int n;              // output columns of this segment
-  int kind;           // GEMM_PLAIN / GEMM_HEADS / GEMM_SWISH
-  void *out;          // bf16
-  long long ld;       // row stride of out (PLAIN, SWISH)
-  int L, H, dh;       // HEADS: rows are (b, l) with l < L; columns (h, j) with j < dh
-};
-struct GemmArgs {
-  const uint16_t *A;  // [M][K]
-  int M, K;
-  int nseg;
-  GemmSeg seg[4];
-  int n_total, ntiles;  // filled by the launcher
-};
-hipError_t launch_gemm_bf16(const GemmArgs &args, hipStream_t st);
-
 // Plain bf16 GEMM through hipBLASLt (blaslt.hip): C[t][n] = sum_k X[t][k] W[n][k]
 // (+ R[t][n] when R is given, same layout as C) for t < T, n < N, row-major with
 // row stride ldc.  hipErrorNotSupported when hipBLASLt has no algorithm for the
@@ -70,9 +50,8 @@ hipError_t blaslt_gemm_nt(const uint16_t *X, const uint16_t *W, uint16_t *C, int
                           void *ws, size_t ws_bytes, hipStream_t st, const uint16_t *R = nullptr);
 
 // Row-wise bf16 passes of the residual block (block.hip): LayerNorm without
-// affine (y may alias x), exact gelu in place, and c += r.
+// affine (y may alias x) and exact gelu in place.
 hipError_t launch_layernorm_bf16(const uint16_t *x, uint16_t *y, long long rows, int d, float eps, hipStream_t st);
 hipError_t launch_gelu_bf16(uint16_t *x, long long n, hipStream_t st);
-hipError_t launch_add_bf16(uint16_t *c, const uint16_t *r, long long n, hipStream_t st);
 
 }  // namespace ret

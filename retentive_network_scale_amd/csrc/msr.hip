@@ -5,14 +5,14 @@
 //   MSR(X) = (swish(X W_G) (.) Y) W_O
 // Launch sequence on the caller's stream:
 //   1. four plain GEMMs X W_Q, X W_K, X W_V, X W_G into one token-major bf16
-//      buffer P[B*L][2 H dk + 2 H dv] (hipBLASLt; this library's GEMM kernel when
-//      hipBLASLt has no algorithm for a shape);
+//      buffer P[B*L][2 H dk + 2 H dv] (hipBLASLt);
 //   2. chunkwise retention (MFMA kernels) reading Q, K, V and the gate straight
 //      from P through strides, with the per-(token, head) GroupNorm and the swish
 //      gate applied in the epilogue -> Z bf16 token-major [B*L, H*dv];
 //   3. GEMM Z . W_O -> y [B*L, d_model] bf16 (as in 1).
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "common.hpp"
@@ -47,22 +47,11 @@ MsrLayout msr_layout(int B, int L, int H, int dk, int dv, int chunk) {
   return m;
 }
 
-// C[t][n] = sum_k X[t][k] W[n][k] (+ R[t][n]) (row stride ldc): hipBLASLt, else
-// this library's GEMM kernel (and a separate add for R, which then has ldc == N).
+// C[t][n] = sum_k X[t][k] W[n][k] (+ R[t][n]) (row stride ldc) through hipBLASLt;
+// hipErrorNotSupported when hipBLASLt offers no algorithm for the shape.
 hipError_t plain_gemm(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, int N, int K, int ldc, void *blas_ws,
                       hipStream_t st, const uint16_t *R = nullptr) {
-  hipError_t e = blaslt_gemm_nt(X, W, C, T, N, K, ldc, blas_ws, BLAS_WS, st, R);
-  if (e != hipErrorNotSupported) return e;
-  GemmArgs g;
-  memset(&g, 0, sizeof(g));
-  g.A = X;
-  g.M = T;
-  g.K = K;
-  g.nseg = 1;
-  g.seg[0] = GemmSeg{W, N, GEMM_PLAIN, C, (long long)ldc, 0, 0, 0};
-  e = launch_gemm_bf16(g, st);
-  if (e != hipSuccess || !R) return e;
-  return launch_add_bf16(C, R, (long long)T * N, st);
+  return blaslt_gemm_nt(X, W, C, T, N, K, ldc, blas_ws, BLAS_WS, st, R);
 }
 
 // P[T][NP] = X [W_Q|W_K|W_V|W_G]^T.  When the four weights sit back to back in
@@ -94,6 +83,15 @@ hipError_t projections(const uint16_t *X, const void *w_q, const void *w_k, cons
 // Defined in abi.hip: records the message returned by retention_last_error().
 ret_status_t retention_fail_(ret_status_t s, const char *msg);
 
+// Status of a failed launch sequence: a GEMM shape for which hipBLASLt offers no
+// algorithm is UNSUPPORTED (nothing of the call was enqueued after it), anything
+// else a HIP error.
+static ret_status_t launch_fail(hipError_t e) {
+  if (e == hipErrorNotSupported)
+    return retention_fail_(RET_ERR_UNSUPPORTED, "hipBLASLt offers no algorithm for one of the GEMM shapes");
+  return launch_fail(e);
+}
+
 // The layer on validated arguments: y = MSR(x) (+ residual, same layout as y).
 static ret_status_t msr_forward(const void *x, const void *w_q, const void *w_k, const void *w_v, const void *w_g,
                          const void *w_o, void *y, const uint16_t *residual, int B, int L, int d_model, int H, int dk,
@@ -108,7 +106,7 @@ static ret_status_t msr_forward(const void *x, const void *w_q, const void *w_k,
   {
     hipError_t e = projections((const uint16_t *)x, w_q, w_k, w_v, w_g, proj, (int)T, d_model, H, dk, dv,
                                ws + m.blas, st);
-    if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+    if (e != hipSuccess) return launch_fail(e);
   }
 
   // 2. chunkwise retention with GroupNorm and the swish gate in the epilogue -> Z
@@ -149,11 +147,11 @@ static ret_status_t msr_forward(const void *x, const void *w_q, const void *w_k,
     for (int i = 0; i < dk / 2; ++i) a.theta[i] = theta[i];
   const ChunkPlan plan = chunk_plan(B, H, L, dk, dv, chunk);
   hipError_t e = launch_mfma_chunkwise(a, plan, ws + m.cw, nullptr, nullptr, st);
-  if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  if (e != hipSuccess) return launch_fail(e);
 
   // 3. output projection
   e = plain_gemm(z, (const uint16_t *)w_o, (uint16_t *)y, (int)T, d_model, H * dv, d_model, ws + m.blas, st, residual);
-  if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  if (e != hipSuccess) return launch_fail(e);
   return retention_fail_(RET_OK, "");
 }
 
@@ -162,7 +160,8 @@ extern "C" {
 
 size_t msr_layer_fwd_workspace_bytes(int B, int L, int d_model, int H, int dk, int dv, int chunk) {
   if (B <= 0 || L <= 0 || d_model <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
-  if (!mfma_supported(dk, dv)) return 0;
+  if (!mfma_supported(dk, dv) || (long long)B * H * L > RETENTION_MAX_TOKEN_HEADS) return 0;
+  chunk = std::min(chunk, L);
   return msr_layout(B, L, H, dk, dv, chunk).total;
 }
 
@@ -183,7 +182,10 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
   }
   if (!(gn_eps >= 0.0f) || !std::isfinite(gn_eps))
     return retention_fail_(RET_ERR_INVALID_ARG, "gn_eps must be finite and >= 0 (the layer always normalises)");
-  if (pos0 < 0 || pos0 > (1LL << 52) - (long long)L) return retention_fail_(RET_ERR_INVALID_ARG, "pos0 out of range");
+  if (pos0 < 0 || pos0 > RETENTION_POS_LIMIT - (long long)L)
+    return retention_fail_(RET_ERR_INVALID_ARG, "pos0 outside [0, 2^31 - L]");
+  if ((long long)B * H * L > RETENTION_MAX_TOKEN_HEADS) return retention_fail_(RET_ERR_UNSUPPORTED, "B*H*L too large");
+  chunk = std::min(chunk, std::max(L, 1));
   if (!mfma_supported(dk, dv))
     return retention_fail_(RET_ERR_UNSUPPORTED, "(dk, dv) has no MFMA kernel");
   if (d_model % 128 || (H * dk) % 128 || (H * dv) % 128)
@@ -262,7 +264,7 @@ ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, con
   // 1. projections of this step's tokens into P[B][NP]
   {
     hipError_t e = projections((const uint16_t *)x, w_q, w_k, w_v, w_g, proj, B, d_model, H, dk, dv, blas, st);
-    if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+    if (e != hipSuccess) return launch_fail(e);
   }
 
   // 2. retention step with GroupNorm and the swish gate -> Z[B][H*dv]
@@ -301,21 +303,22 @@ ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, con
   if (theta)
     for (int i = 0; i < dk / 2; ++i) a.theta[i] = theta[i];
   hipError_t e = launch_vec_step(a, state, pos, st);
-  if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  if (e != hipSuccess) return launch_fail(e);
 
   // 3. output projection, 4. positions
   e = plain_gemm(z, (const uint16_t *)w_o, (uint16_t *)y, B, d_model, H * dv, d_model, blas, st);
-  if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  if (e != hipSuccess) return launch_fail(e);
   if (advance_pos) {
     e = launch_advance_pos(pos, B, st);
-    if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+    if (e != hipSuccess) return launch_fail(e);
   }
   return retention_fail_(RET_OK, "");
 }
 
 size_t retnet_block_fwd_workspace_bytes(int B, int L, int d_model, int H, int dk, int dv, int d_ffn, int chunk) {
   if (B <= 0 || L <= 0 || d_model <= 0 || H <= 0 || dk <= 0 || dv <= 0 || d_ffn <= 0 || chunk <= 0) return 0;
-  if (!mfma_supported(dk, dv)) return 0;
+  if (!mfma_supported(dk, dv) || (long long)B * H * L > RETENTION_MAX_TOKEN_HEADS) return 0;
+  chunk = std::min(chunk, L);
   const size_t T = (size_t)B * L;
   return 2 * align256(T * d_model * 2) + align256(T * d_ffn * 2) + msr_layout(B, L, H, dk, dv, chunk).total;
 }
@@ -341,7 +344,10 @@ ret_status_t retnet_block_fwd(const void *x, const void *w_q, const void *w_k, c
   }
   if (!(gn_eps >= 0.0f) || !std::isfinite(gn_eps) || !(ln_eps >= 0.0f) || !std::isfinite(ln_eps))
     return retention_fail_(RET_ERR_INVALID_ARG, "gn_eps and ln_eps must be finite and >= 0");
-  if (pos0 < 0 || pos0 > (1LL << 52) - (long long)L) return retention_fail_(RET_ERR_INVALID_ARG, "pos0 out of range");
+  if (pos0 < 0 || pos0 > RETENTION_POS_LIMIT - (long long)L)
+    return retention_fail_(RET_ERR_INVALID_ARG, "pos0 outside [0, 2^31 - L]");
+  if ((long long)B * H * L > RETENTION_MAX_TOKEN_HEADS) return retention_fail_(RET_ERR_UNSUPPORTED, "B*H*L too large");
+  chunk = std::min(chunk, std::max(L, 1));
   if (!mfma_supported(dk, dv)) return retention_fail_(RET_ERR_UNSUPPORTED, "(dk, dv) has no MFMA kernel");
   if (d_model % 128 || (H * dk) % 128 || (H * dv) % 128 || d_ffn % 128 || d_model > 8192)
     return retention_fail_(RET_ERR_UNSUPPORTED,
@@ -367,7 +373,7 @@ ret_status_t retnet_block_fwd(const void *x, const void *w_q, const void *w_k, c
   uint16_t *u = (uint16_t *)(ws + 2 * align256(T * d_model * 2));
   char *mws = ws + 2 * align256(T * d_model * 2) + align256(T * d_ffn * 2);
   hipError_t e = launch_layernorm_bf16((const uint16_t *)x, h, (long long)T, d_model, ln_eps, st);
-  if (e != hipSuccess) return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+  if (e != hipSuccess) return launch_fail(e);
   ret_status_t s = msr_forward(h, w_q, w_k, w_v, w_g, w_o, yb, (const uint16_t *)x, B, L, d_model, H, dk, dv, chunk,
                                gamma, theta, pos0, gn_eps, mws, msr_layout(B, L, H, dk, dv, chunk), st);
   if (s != RET_OK) return s;
@@ -377,7 +383,7 @@ ret_status_t retnet_block_fwd(const void *x, const void *w_q, const void *w_k, c
       (e = launch_gelu_bf16(u, (long long)T * d_ffn, st)) != hipSuccess ||
       (e = plain_gemm(u, (const uint16_t *)w_2, (uint16_t *)out, (int)T, d_model, d_ffn, d_model, blas, st, yb)) !=
           hipSuccess)
-    return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
+    return launch_fail(e);
   return retention_fail_(RET_OK, "");
 }
 

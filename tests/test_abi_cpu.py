@@ -184,3 +184,41 @@ def test_block_rejects():
     assert call(ln_eps=-1.0) == INVALID
     assert call(w_1=None) == INVALID
     assert call(wsb=need - 1) == WORKSPACE
+
+
+@pytest.mark.parametrize("B,H,L,dk,dv,ind", [(1, 8, 32768, 128, 256, BF16), (4, 8, 4096, 256, 512, BF16),
+                                            (1, 2, 200, 16, 16, F32), (2, 8, 700, 256, 512, BF16)])
+def test_chunk_longer_than_sequence_is_the_sequence(B, H, L, dk, dv, ind):
+    """A chunk longer than L plans exactly like chunk = L (one chunk), with no int
+    overflow in the planning arithmetic, for every query that takes a chunk size."""
+    lib = rn.lib()
+    big = (2 ** 31 - 1, 4 * L, L + 1)
+    ref = lib.retention_chunkwise_workspace_bytes(B, H, L, dk, dv, L, ind)
+    assert ref > 0
+    for c in big:
+        assert lib.retention_chunkwise_workspace_bytes(B, H, L, dk, dv, c, ind) == ref, c
+    ref = lib.retention_chunkwise_bwd_workspace_bytes(B, H, L, dk, dv, L, ind)
+    for c in big:
+        assert lib.retention_chunkwise_bwd_workspace_bytes(B, H, L, dk, dv, c, ind) == ref, c
+    if ind == BF16:
+        dm = 2048
+        ref = lib.msr_layer_fwd_workspace_bytes(B, L, dm, H, dk, dv, L)
+        assert ref > 0
+        for c in big:
+            assert lib.msr_layer_fwd_workspace_bytes(B, L, dm, H, dk, dv, c) == ref, c
+            assert (lib.retnet_block_fwd_workspace_bytes(B, L, dm, H, dk, dv, 4096, c) ==
+                    lib.retnet_block_fwd_workspace_bytes(B, L, dm, H, dk, dv, 4096, L)), c
+
+
+def test_position_and_size_limits():
+    """Positions are int32 (pos0 + L <= 2^31); at most 2^28 token-heads per call."""
+    assert _par(pos0=2 ** 31 - 7) == INVALID
+    assert _par(pos0=2 ** 40) == INVALID
+    assert b"2^31" in rn.lib().retention_last_error()
+    assert _par(B=2 ** 14, H=2, L=2 ** 14, gamma=_f([0.9, 0.5])) == UNSUPPORTED
+    lib = rn.lib()
+    assert lib.retention_chunkwise_workspace_bytes(2 ** 14, 2, 2 ** 14, 128, 256, 256, BF16) == 0
+    g = _f([0.9] * 2)
+    r = lib.msr_layer_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, 1, 8, 256, 2, 128, 256, 8, g, None, 2 ** 31 - 7,
+                          1e-5, None, 0, None)
+    assert r == INVALID

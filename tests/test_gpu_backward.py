@@ -54,11 +54,9 @@ def test_backward_bf16(dk, dv, L, chunk, rot, pos0):
 
 def test_backward_32k_sampled_rows():
     """The long-context workload (B1 H8 L32768 dk128 dv256, chunk 256) with a seeded
-    output gradient: sampled rows of dq, dk and dv against the oracle's sums.  The
-    sampled rows are compared as one set, normalised as a (b, h) slice is: a row
-    whose sum has a single term (dv of the last token is (q~ . k~) dO) carries the
-    relative rounding error of one bf16 score, which alone can exceed the bar when
-    that score is small."""
+    output gradient: ten sampled rows of dq, dk and dv in each of three heads (the
+    fastest and slowest decay and one between) against the oracle's sums, compared
+    per head -- the rows of one head form one slice of the tolerance metric."""
     wl = CHUNKWISE_32K
     q, k, v = wl.qkv()
     do = randn((wl.B, wl.H, wl.L, wl.dv), 3009, 1.0, torch.bfloat16)
@@ -66,10 +64,11 @@ def test_backward_32k_sampled_rows():
     got = rn.retention_chunkwise_bwd(*(t.to(DEV) for t in (q, k, v, do)), g, wl.chunk, th)
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
-    idx = [(0, 0, 0), (0, 7, wl.L - 1), (0, 3, 255), (0, 3, 256), (0, 5, 16384)]
-    idx += [(0, int(rng.integers(wl.H)), int(rng.integers(wl.L))) for _ in range(5)]
+    heads, per = (0, 3, 7), 10
+    fixed = [0, 255, 256, 16384, wl.L - 1]
+    idx = [(0, h, n) for h in heads for n in fixed + [int(x) for x in rng.integers(wl.L, size=per - len(fixed))]]
     qn, kn, vn, don = (oracle.as_f64(t) for t in (q, k, v, do))
     for name, t in zip("qkv", got):
-        ref = oracle.backward_rows(qn, kn, vn, don, g, name, idx, th)
-        gotr = np.stack([t[b, h, n].float().cpu().numpy() for b, h, n in idx])
-        _tol.assert_bf16(gotr, ref, slice_dims=0, what=f"d{name} sampled rows")
+        ref = oracle.backward_rows(qn, kn, vn, don, g, name, idx, th).reshape(len(heads), per, -1)
+        gotr = np.stack([t[b, h, n].float().cpu().numpy() for b, h, n in idx]).reshape(len(heads), per, -1)
+        _tol.assert_bf16(gotr, ref, slice_dims=1, what=f"d{name} sampled rows, per head")

@@ -166,3 +166,46 @@ def test_chunkwise_gn_rot_graph_replay():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager[i]), f"replay {i} differs from the eager call"
+
+
+@pytest.mark.parametrize("dk,dv,L,chunk", [(256, 512, 300, 4096), (128, 256, 200, 2 ** 31 - 1)])
+def test_chunk_longer_than_sequence(dk, dv, L, chunk):
+    """A chunk longer than the sequence is one chunk (the parallel form): the
+    (256, 512) pair takes the query-block path, (128, 256) the segment path."""
+    B, H = 1, 2
+    q, k, v = _qkv(B, H, L, dk, dv, 400 + dk)
+    g, th = torch.tensor([0.97, 0.6], dtype=torch.float32), rotation_theta(dk)
+    ref_o, ref_s = oracle.recurrent(q, k, v, g, th, pos0=3)
+    o, s = rn.retention_chunkwise(*_gpu(q, k, v), g, chunk, th, pos0=3, state_out=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _tol.assert_bf16(o, ref_o, what=f"chunk {chunk} > L={L}")
+    _tol.assert_bf16(s, ref_s, what="final state")
+
+
+@pytest.mark.parametrize("form", ["parallel", "chunkwise", "step"])
+def test_rotation_at_the_position_cap(form):
+    """The last positions a call may use (pos0 + L = 2^31): the rotation angle
+    p theta_i is reduced in fp64 before the fp32 sine and cosine, so outputs keep
+    the bf16 bar there (the pages' e^{i n theta} at n near 2^31)."""
+    dk, dv, H = 128, 256, 2
+    L = 1 if form == "step" else 150
+    pos0 = 2 ** 31 - L
+    q, k, v = _qkv(1, H, L, dk, dv, 500)
+    g, th = torch.tensor([0.9, 0.5], dtype=torch.float32), rotation_theta(dk)
+    s0 = randn((1, H, dk, dv), 501, 0.3)
+    ref_o, ref_s = oracle.recurrent(q, k, v, g, th, pos0=pos0, s_in=s0)
+    if form == "parallel":
+        ref_o, _ = oracle.recurrent(q, k, v, g, th, pos0=pos0)
+        o = rn.retention_parallel(*_gpu(q, k, v), g, th, pos0=pos0, out_dtype=torch.float32)
+    elif form == "chunkwise":
+        o, s = rn.retention_chunkwise(*_gpu(q, k, v, ), g, 64, th, pos0=pos0, state_in=s0.to(DEV), state_out=True,
+                                      out_dtype=torch.float32)
+    else:
+        s = s0.to(DEV)
+        pos = torch.full((1,), pos0, dtype=torch.int32, device=DEV)
+        o = rn.retention_recurrent_step(*_gpu(q[:, :, 0], k[:, :, 0], v[:, :, 0]), s, pos, g, th,
+                                        out_dtype=torch.float32)[:, :, None]
+    torch.cuda.synchronize()
+    _tol.assert_bf16(o, ref_o, what=f"{form} at positions {pos0}..{pos0 + L - 1}")
+    if form != "parallel":
+        _tol.assert_bf16(s, ref_s, what="state")

@@ -28,7 +28,7 @@ def _case(seed):
     L = int(r.integers(1, 400))
     chunk = int(r.integers(16, 321))
     gamma = torch.tensor([GAMMAS[int(i)] for i in r.integers(len(GAMMAS), size=H)], dtype=torch.float32)
-    pos0 = int(r.integers(0, 2 ** 31))
+    pos0 = min(int(r.integers(0, 2 ** 31)), 2 ** 31 - L)  # positions are int32: pos0 + L <= 2^31
     rot, gn = bool(r.integers(2)), bool(r.integers(2))
     odt = torch.float32 if r.integers(2) else torch.bfloat16
     with_state = bool(r.integers(2))
@@ -79,6 +79,7 @@ def test_random_fp32_vector_path(seed):
     dk, dv = 2 * int(r.integers(1, 49)), 4 * int(r.integers(1, 33))
     B, H, L = int(r.integers(1, 3)), int(r.integers(1, 4)), int(r.integers(1, 200))
     chunk, g, pos0 = int(r.integers(1, 130)), _gammas(r, H), int(r.integers(0, 2 ** 31))
+    pos0 = min(pos0, 2 ** 31 - L)
     th = rotation_theta(dk) if r.integers(2) else None
     eps = 1e-5 if r.integers(2) else None
     s0 = randn((B, H, dk, dv), 5100 + seed, 0.5) if r.integers(2) else None
@@ -143,6 +144,7 @@ def test_random_backward(seed):
     dk, dv = [(64, 128), (128, 128), (128, 256)][int(r.integers(3))]
     B, H, L = 1, int(r.integers(1, 4)), int(r.integers(1, 300))
     chunk, g, pos0 = int(r.integers(16, 300)), _gammas(r, H), int(r.integers(0, 2 ** 31))
+    pos0 = min(pos0, 2 ** 31 - L)
     th = rotation_theta(dk) if r.integers(2) else None
     q = randn((B, H, L, dk), 7100 + seed, dk ** -0.5, torch.bfloat16)
     k = randn((B, H, L, dk), 7200 + seed, dk ** -0.5, torch.bfloat16)
@@ -168,6 +170,7 @@ def test_random_msr_layer(seed):
         H = 2
     B, L = int(r.integers(1, 3)), int(r.integers(1, 300))
     chunk, pos0 = int(r.integers(16, 300)), int(r.integers(0, 2 ** 31))
+    pos0 = min(pos0, 2 ** 31 - L)
     g = multiscale_gamma(H)
     th = rotation_theta(dk)
     x = randn((B, L, dm), 8100 + seed, 1.0, torch.bfloat16)

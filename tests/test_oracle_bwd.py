@@ -74,3 +74,20 @@ def test_rows_match_full():
         got = oracle.backward_rows(q, k, v, do, GAMMA, w, idx, THETA, 2)
         ref = np.stack([full[w][b, h, n] for b, h, n in idx])
         assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), w
+
+
+@pytest.mark.parametrize("L,pos0,rot", [(1, 0, True), (29, 7, True), (40, 0, False)])
+def test_recurrent_adjoint_matches_double_sum(L, pos0, rot):
+    """The adjoint of the recurrent form (forward sweep of the state for dq, reverse
+    sweep for dk and dv) and the double sum over n >= m are two independent
+    derivations of the same gradients; they agree to rounding, including a head
+    with gamma = 0 (only n = m) and one with gamma = 1 (no decay)."""
+    B, H, dk, dv = 2, 3, 6, 5
+    q, k, v, do = _inputs(B, H, L, dk, dv, 10 + L)
+    g = np.array([0.0, 1.0, 0.83])
+    th = THETA if rot else None
+    ref = oracle.backward(q, k, v, do, g, th, pos0)
+    got = oracle.backward_recurrent(q, k, v, do, g, th, pos0)
+    for name, a, b in zip("qkv", got, ref):
+        err = np.abs(a - b).max() / max(np.abs(b).max(), 1e-300)
+        assert err < 1e-12, f"d{name}: {err:.2e}"
