@@ -119,6 +119,27 @@ ret_status_t retention_chunkwise(const void *q, const void *k, const void *v, vo
                                  void *hip_stream);
 
 /*
+ * retention_chunkwise without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same computation, arguments (less the workspace) and
+ * errors as retention_chunkwise; the call allocates nothing.  Its scratch is a
+ * device array inside the library, RETENTION_NOALLOC_SCRATCH_BYTES on each GPU
+ * it runs on, held until the process ends.  UNSUPPORTED when
+ * retention_chunkwise_workspace_bytes() of the same arguments exceeds that size
+ * (B1 H8 L32768 dk128 dv256 chunk 256 needs 32 MiB).  Every call on a GPU uses
+ * that GPU's one array and it keeps the last call's contents (nothing in it needs
+ * clearing): calls that overlap on one GPU -- other streams, other host threads
+ * -- race, so the caller serialises them.  Every launch stays on hip_stream.
+ */
+#define RETENTION_NOALLOC_SCRATCH_BYTES (64u << 20)
+ret_status_t retention_chunkwise_noalloc(const void *q, const void *k, const void *v, void *o, int B,
+                                         int H, int L, int dk, int dv, int chunk,
+                                         const float *gamma, const float *theta, long long pos0,
+                                         const float *state_in, float *state_out, float gn_eps,
+                                         ret_dtype_t in_dtype, ret_dtype_t out_dtype,
+                                         void *hip_stream);
+
+/*
  * One recurrent step (Sec. 2.1 (2); the custom operator for the state update
  * of "RetNet dual-mode hands-on manual" Sec. 4.2):
  *   S <- gamma_h S + k_rot^T v   (rank-1 update of the dk x dv state)

@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "RetentionError", "lib", "retention_parallel", "retention_chunkwise",
-    "retention_chunkwise_workspace_bytes", "retention_recurrent_step", "msr_layer_fwd",
+    "retention_chunkwise_workspace_bytes", "retention_chunkwise_noalloc", "retention_recurrent_step",
+    "msr_layer_fwd",
     "msr_layer_fwd_workspace_bytes", "msr_layer_step", "msr_layer_step_workspace_bytes",
     "retention_chunkwise_bwd", "retention_chunkwise_bwd_workspace_bytes", "retnet_block_fwd",
     "retnet_block_fwd_workspace_bytes", "LIB_PATH",
@@ -40,6 +41,8 @@ _SIGS = {
     "retention_chunkwise_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "retention_chunkwise": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _fp, _fp, _ll, _vp, _vp,
                                  _f, _i, _i, _vp, _sz, _vp]),
+    "retention_chunkwise_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _fp, _fp, _ll, _vp, _vp,
+                                         _f, _i, _i, _vp]),
     "retention_recurrent_step": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _fp, _fp, _vp, _f, _i,
                                       _i, _vp]),
     "retention_chunkwise_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
@@ -175,6 +178,34 @@ def retention_chunkwise(q, k, v, gamma, chunk, theta=None, pos0=0, state_in=None
     _check(lib().retention_chunkwise(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "o"), B, H, L, dk,
                                      dv, int(chunk), gp, thp, int(pos0), sin, sout, _eps(gn_eps), _dt(q),
                                      _dt(out), ws, wsb, _stream(stream)))
+    return out, state_out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # RETENTION_NOALLOC_SCRATCH_BYTES of the C header
+
+
+def retention_chunkwise_noalloc(q, k, v, gamma, chunk, theta=None, pos0=0, state_in=None, state_out=None,
+                                gn_eps=None, out_dtype=None, out=None, stream=None):
+    """retention_chunkwise with the library's own device scratch instead of a
+    workspace: the C call allocates nothing.  `out` and a `state_out` tensor should
+    be passed by callers that cannot allocate (as under graph capture); with None /
+    True they are allocated here, before the call.  Returns (o, state_out)."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    odt = _dt(q) if out_dtype is None else _dt(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=_torch_dt(odt), device=q.device)
+    if state_out is True:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif state_out is False:
+        state_out = None
+    g, gp = _host_f32(gamma, H, "gamma")
+    th, thp = _host_f32(theta, dk // 2, "theta")
+    sin = None if state_in is None else _dev(state_in, "state_in")
+    sout = None if state_out is None else _dev(state_out, "state_out")
+    _check(lib().retention_chunkwise_noalloc(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "o"), B, H, L, dk,
+                                             dv, int(chunk), gp, thp, int(pos0), sin, sout, _eps(gn_eps), _dt(q),
+                                             _dt(out), _stream(stream)))
     return out, state_out
 
 

@@ -6,6 +6,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -252,12 +254,17 @@ size_t retention_chunkwise_workspace_bytes(int B, int H, int L, int dk, int dv, 
   return vec_chunk_ws(B, H, dk, dv);
 }
 
-ret_status_t retention_chunkwise(const void *q, const void *k, const void *v, void *o, int B, int H,
-                                 int L, int dk, int dv, int chunk, const float *gamma,
-                                 const float *theta, long long pos0, const float *state_in,
-                                 float *state_out, float gn_eps, ret_dtype_t in_dtype,
-                                 ret_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
-                                 void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The chunkwise call on a given workspace.  fork: whether a small launch may use
+// the library's second stream (the allocation-free entry point keeps every launch
+// on the caller's stream).
+ret_status_t chunkwise_impl(const void *q, const void *k, const void *v, void *o, int B, int H, int L, int dk, int dv,
+                            int chunk, const float *gamma, const float *theta, long long pos0, const float *state_in,
+                            float *state_out, float gn_eps, ret_dtype_t in_dtype, ret_dtype_t out_dtype,
+                            void *workspace, size_t workspace_bytes, void *hip_stream, bool fork) {
   ret_status_t s = check_common(B, H, L, dk, dv, gamma, theta, pos0, gn_eps, in_dtype, out_dtype);
   if (s != RET_OK) return s;
   if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk=%d must be positive", chunk);
@@ -289,7 +296,7 @@ ret_status_t retention_chunkwise(const void *q, const void *k, const void *v, vo
     if (plan.ws_bytes && (!workspace || workspace_bytes < plan.ws_bytes))
       return fail(RET_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes, workspace_bytes);
     if (workspace && !aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    return hip_status(launch_mfma_chunkwise(a, plan, workspace, state_in, state_out, st));
+    return hip_status(launch_mfma_chunkwise(a, plan, workspace, state_in, state_out, st, fork));
   }
   // vector path: the running state lives in state_out when given, else in the workspace
   float *S = state_out;
@@ -301,6 +308,70 @@ ret_status_t retention_chunkwise(const void *q, const void *k, const void *v, vo
     S = (float *)workspace;
   }
   return hip_status(launch_vec_chunkwise(a, S, state_in, st));
+}
+
+// Scratch of the allocation-free chunkwise entry point: a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never uses
+// its name as an address (in host code it is only a stand-in for the symbol):
+// the device address comes from hipGetSymbolAddress, once per device with that
+// device current, and is kept per device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)RETENTION_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_ptr;
+
+// This device's address of `scratch` (nullptr and the error on failure).
+void *scratch_ptr(hipError_t *err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) return it->second;
+  void *ptr = nullptr;
+  *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess || !ptr) {
+    if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  g_scratch_ptr.emplace(dev, ptr);
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+ret_status_t retention_chunkwise(const void *q, const void *k, const void *v, void *o, int B, int H,
+                                 int L, int dk, int dv, int chunk, const float *gamma,
+                                 const float *theta, long long pos0, const float *state_in,
+                                 float *state_out, float gn_eps, ret_dtype_t in_dtype,
+                                 ret_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream) {
+  return chunkwise_impl(q, k, v, o, B, H, L, dk, dv, chunk, gamma, theta, pos0, state_in, state_out, gn_eps, in_dtype,
+                        out_dtype, workspace, workspace_bytes, hip_stream, true);
+}
+
+ret_status_t retention_chunkwise_noalloc(const void *q, const void *k, const void *v, void *o, int B, int H, int L,
+                                         int dk, int dv, int chunk, const float *gamma, const float *theta,
+                                         long long pos0, const float *state_in, float *state_out, float gn_eps,
+                                         ret_dtype_t in_dtype, ret_dtype_t out_dtype, void *hip_stream) {
+  ret_status_t s = check_common(B, H, L, dk, dv, gamma, theta, pos0, gn_eps, in_dtype, out_dtype);
+  if (s != RET_OK) return s;
+  if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk=%d must be positive", chunk);
+  const size_t need = L > 0 ? retention_chunkwise_workspace_bytes(B, H, L, dk, dv, chunk, in_dtype) : 0;
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(RET_ERR_UNSUPPORTED, "needs %zu bytes of scratch, the allocation-free entry point has %zu", need,
+                NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if (need) {
+    hipError_t e = hipSuccess;
+    ws = scratch_ptr(&e);
+    if (!ws) return fail(RET_ERR_HIP, "HIP error: %s (address of the scratch array)", hipGetErrorString(e));
+  }
+  return chunkwise_impl(q, k, v, o, B, H, L, dk, dv, chunk, gamma, theta, pos0, state_in, state_out, gn_eps, in_dtype,
+                        out_dtype, ws, need, hip_stream, false);
 }
 
 size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_t in_dtype) {

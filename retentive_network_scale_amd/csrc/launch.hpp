@@ -39,8 +39,10 @@ ChunkPlan chunk_plan(int B, int H, int L, int dk, int dv, int chunk);
 // Whether chunkwise retention of these dimensions runs design A, the only one
 // that reads reversed inputs (RetArgs::in_rev).
 bool chunk_state_in_regs(int B, int H, int L, int dk, int dv, int chunk);
+// fork: a small first-blocks launch may run on a second stream of the library's
+// own (created on first use); false keeps every launch on st.
 hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &plan, void *ws,
-                                 const float *state_in, float *state_out, hipStream_t st);
+                                 const float *state_in, float *state_out, hipStream_t st, bool fork = true);
 
 // Plain bf16 GEMM through hipBLASLt (blaslt.hip): C[t][n] = sum_k X[t][k] W[n][k]
 // (+ R[t][n] when R is given, same layout as C) for t < T, n < N, row-major with

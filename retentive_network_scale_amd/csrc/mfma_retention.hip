@@ -1544,7 +1544,8 @@ static bool split_all_blocks(const RetArgs &a) {
 }
 
 template <int DK, int DV>
-static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const uint16_t *sinT, hipStream_t st) {
+static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const uint16_t *sinT, hipStream_t st,
+                              bool fork) {
   geo.nqb = par ? (a.L + BT - 1) / BT : (a.chunk + BT - 1) / BT;
   geo.nchunks = par ? 1 : (a.L + a.chunk - 1) / a.chunk;
   geo.ntasks = a.B * a.H * geo.nchunks * geo.nqb;
@@ -1570,7 +1571,7 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
     // chunkwise: the first blocks (one small launch) run on the side stream,
     // beside the rest (measured no faster for the parallel form, whose first
     // blocks take a single short visit)
-    SideStream *ss = par ? nullptr : side_stream();
+    SideStream *ss = (par || !fork) ? nullptr : side_stream();
     std::unique_lock<std::mutex> lock;
     hipStream_t st1 = st;
     if (ss) {
@@ -1604,7 +1605,7 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
 
 template <int DK, int DV>
 static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, const float *state_in,
-                                float *state_out, hipStream_t st) {
+                                float *state_out, hipStream_t st, bool fork) {
   constexpr bool FITS = (long long)DK * DV <= IN_REGS_MAX;  // design A possible
   constexpr int DVW1 = FITS ? DV : (DK * DV > SPLIT_STATE_MAX ? (int)(SPLIT_STATE_MAX / DK) : DV);
   const bool in_regs = FITS && p.in_regs;
@@ -1628,7 +1629,7 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (FITS) {
-    if (!in_regs) return run_qblocks<DK, DV>(a, geo, false, sinT, st);
+    if (!in_regs) return run_qblocks<DK, DV>(a, geo, false, sinT, st, fork);
     geo.ntasks = a.B * a.H * geo.nseg;
     const dim3 grid(xcd_grid(geo.ntasks));
     if ((a.use_gn && a.use_theta) || split_all_blocks(a))
@@ -1639,30 +1640,30 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
       hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, seg);
     return hipGetLastError();
   } else {
-    return run_qblocks<DK, DV>(a, geo, false, sinT, st);
+    return run_qblocks<DK, DV>(a, geo, false, sinT, st, fork);
   }
 }
 
 hipError_t launch_mfma_parallel(const RetArgs &a, hipStream_t st) {
   TaskGeom geo{1, 1, 1, 1, 0, 1};
-  if (a.dk == 64 && a.dv == 128) return run_qblocks<64, 128>(a, geo, true, nullptr, st);
-  if (a.dk == 128 && a.dv == 128) return run_qblocks<128, 128>(a, geo, true, nullptr, st);
-  if (a.dk == 128 && a.dv == 256) return run_qblocks<128, 256>(a, geo, true, nullptr, st);
-  if (a.dk == 256 && a.dv == 128) return run_qblocks<256, 128>(a, geo, true, nullptr, st);
-  if (a.dk == 256 && a.dv == 256) return run_qblocks<256, 256>(a, geo, true, nullptr, st);
-  if (a.dk == 256 && a.dv == 512) return run_qblocks<256, 512>(a, geo, true, nullptr, st);
+  if (a.dk == 64 && a.dv == 128) return run_qblocks<64, 128>(a, geo, true, nullptr, st, false);
+  if (a.dk == 128 && a.dv == 128) return run_qblocks<128, 128>(a, geo, true, nullptr, st, false);
+  if (a.dk == 128 && a.dv == 256) return run_qblocks<128, 256>(a, geo, true, nullptr, st, false);
+  if (a.dk == 256 && a.dv == 128) return run_qblocks<256, 128>(a, geo, true, nullptr, st, false);
+  if (a.dk == 256 && a.dv == 256) return run_qblocks<256, 256>(a, geo, true, nullptr, st, false);
+  if (a.dk == 256 && a.dv == 512) return run_qblocks<256, 512>(a, geo, true, nullptr, st, false);
   return hipErrorNotSupported;
 }
 
 hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &p, void *ws, const float *state_in,
-                                 float *state_out, hipStream_t st) {
+                                 float *state_out, hipStream_t st, bool fork) {
   char *w = (char *)ws;
-  if (a.dk == 64 && a.dv == 128) return run_chunkwise<64, 128>(a, p, w, state_in, state_out, st);
-  if (a.dk == 128 && a.dv == 128) return run_chunkwise<128, 128>(a, p, w, state_in, state_out, st);
-  if (a.dk == 128 && a.dv == 256) return run_chunkwise<128, 256>(a, p, w, state_in, state_out, st);
-  if (a.dk == 256 && a.dv == 128) return run_chunkwise<256, 128>(a, p, w, state_in, state_out, st);
-  if (a.dk == 256 && a.dv == 256) return run_chunkwise<256, 256>(a, p, w, state_in, state_out, st);
-  if (a.dk == 256 && a.dv == 512) return run_chunkwise<256, 512>(a, p, w, state_in, state_out, st);
+  if (a.dk == 64 && a.dv == 128) return run_chunkwise<64, 128>(a, p, w, state_in, state_out, st, fork);
+  if (a.dk == 128 && a.dv == 128) return run_chunkwise<128, 128>(a, p, w, state_in, state_out, st, fork);
+  if (a.dk == 128 && a.dv == 256) return run_chunkwise<128, 256>(a, p, w, state_in, state_out, st, fork);
+  if (a.dk == 256 && a.dv == 128) return run_chunkwise<256, 128>(a, p, w, state_in, state_out, st, fork);
+  if (a.dk == 256 && a.dv == 256) return run_chunkwise<256, 256>(a, p, w, state_in, state_out, st, fork);
+  if (a.dk == 256 && a.dv == 512) return run_chunkwise<256, 512>(a, p, w, state_in, state_out, st, fork);
   return hipErrorNotSupported;
 }
 
