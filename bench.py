@@ -40,19 +40,33 @@ def _settle(fn, seconds=SETTLE_S):
         torch.cuda.synchronize()
 
 
+_LAST_CALLS = []  # per-call seconds of the latest _time_calls (event pairs between consecutive calls)
+
+
 def _time_calls(fn, steps, warmup):
+    """Seconds for `steps` back-to-back calls, between two events on the stream the
+    calls run on (torch's current stream, which the library is given).  An event
+    after every call also gives per-call times (_LAST_CALLS) for the median and min."""
     import torch
     _settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    stop.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / 1000.0  # seconds for all steps
+    _LAST_CALLS[:] = [ev[i].elapsed_time(ev[i + 1]) / 1000.0 for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / 1000.0  # seconds for all steps
+
+
+def _spread():
+    """Median and min per-call milliseconds of the latest timed loop."""
+    import statistics
+    c = _LAST_CALLS
+    return {"median_ms": statistics.median(c) * 1e3, "min_ms": min(c) * 1e3, "calls_timed": len(c)} if c else {}
 
 
 def _read_traffic(name):
@@ -123,8 +137,9 @@ def bench_chunkwise(steps, warmup):
     flops_alg = wl.B * wl.H * (wl.L / C) * 2 * (C * (C + 1) / 2 * (wl.dk + wl.dv) + 2 * C * wl.dk * wl.dv)
     achieved = bytes_alg / per_call / 1e9
     traffic = _read_traffic("chunkwise_32k")
+    spread = _spread()
     return {
-        "tokens_per_s": tokens / per_call, "ms_per_step": per_call * 1e3, "tokens": tokens,
+        "tokens_per_s": tokens / per_call, "ms_per_step": per_call * 1e3, "tokens": tokens, **spread,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "retention_chunkwise call: seg_state_kernel + seg_scan_kernel + seg_out_kernel (durations summed)",
@@ -150,12 +165,12 @@ def bench_chunkwise_bwd(steps, warmup):
     t = _time_calls(lambda: rn.retention_chunkwise_bwd(q, k, v, do, g, wl.chunk, th, out=outs, workspace=ws),
                     steps, warmup)
     per_call = t / steps
-    # algorithmic: q, k, v, dO read once; dq, dk, dv written once (bf16)
-    bytes_alg = 2 * wl.B * wl.H * wl.L * (2 * wl.dk + 2 * wl.dv) + 2 * wl.B * wl.H * wl.L * (2 * wl.dk + wl.dv)
+    spread = _spread()
+    bytes_alg = _alg_bytes_bwd()
     achieved = bytes_alg / per_call / 1e9
-    return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3,
+    return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3, **spread,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": _read_traffic("chunkwise_bwd"),
                          "kernel": "retention_chunkwise_bwd call: rotate/reverse passes, three chunkwise "
                                    "retentions writing the gradients through an un-rotating, reversing epilogue",
                          "algorithmic_bytes_per_call": bytes_alg}}
@@ -181,7 +196,7 @@ def bench_chunk_sweep(steps, warmup):
                          dtype=torch.uint8, device="cuda")
         t = _time_calls(lambda: rn.retention_chunkwise(q, k, v, g, chunk, th, state_out=state, out=out,
                                                        workspace=ws), steps, warmup)
-        res[str(chunk)] = {"tokens_per_s": wl.B * wl.L * steps / t, "ms_per_step": t / steps * 1e3}
+        res[str(chunk)] = {"tokens_per_s": wl.B * wl.L * steps / t, "ms_per_step": t / steps * 1e3, **_spread()}
     return res
 
 
@@ -231,7 +246,7 @@ def bench_parallel(steps, warmup):
     per_call = t / steps
     flops = 2 * wl.B * wl.H * wl.L * (wl.L + 1) / 2 * (wl.dk + wl.dv)
     tf = flops / per_call / 1e12
-    return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3,
+    return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3, **_spread(),
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / BF16_PEAK_TFLOPS, "traffic": _read_traffic("parallel_2k"),
                          "kernel": "qblock_kernel<256,512,parallel> (hi+lo scores for the first query block of each sequence, bf16 for the rest)",
@@ -257,9 +272,9 @@ def bench_msr(steps, warmup):
     gemm = 2 * T * wl.d_model * (2 * wl.H * wl.dk + 2 * wl.H * wl.dv) + 2 * T * wl.H * wl.dv * wl.d_model
     ret = T * wl.H * ((C + 1) * (wl.dk + wl.dv) + 4 * wl.dk * wl.dv)
     tf = (gemm + ret) / per_call / 1e12
-    return {"tokens_per_s": T / per_call, "ms_per_step": per_call * 1e3,
+    return {"tokens_per_s": T / per_call, "ms_per_step": per_call * 1e3, **_spread(),
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": _read_traffic("msr_layer"),
                          "kernel": "msr_layer_fwd (GEMM, chunkwise retention, GroupNorm+gate, GEMM)",
                          "algorithmic_tflop_per_call": (gemm + ret) / 1e12}}
 
@@ -283,11 +298,38 @@ def copy_calibration(reps=3):
 # (kernels summed per call, kernel that occurs exactly once per call).  The
 # parallel form launches two query-block kernels per call (its hi+lo first
 # blocks, SPLIT = true, and the rest): only the second counts the calls.
+# The gated layer's legs also count the hipBLASLt GEMM kernels (names start with
+# Cijk / Custom_Cijk); the backward counts calls by its one (dk, dv) = (128, 256)
+# retention.
 _PMC_GROUPS = {
-    "chunkwise_32k": ("ret::", ("seg_out_kernel",)),
-    "decode_step": ("vec_step_kernel", ("vec_step_kernel",)),
-    "parallel_2k": ("qblock_kernel", ("qblock_kernel<256, 512, true, false>",)),
+    "chunkwise_32k": (("ret::",), ("seg_out_kernel",)),
+    "decode_step": (("vec_step_kernel",), ("vec_step_kernel",)),
+    "parallel_2k": (("qblock_kernel",), ("qblock_kernel<256, 512, true, false>",)),
+    "chunkwise_bwd": (("ret::",), ("seg_state_kernel<128, 256>",)),
+    "msr_layer": (("ret::", "Cijk"), ("seg_scan_t_kernel",)),
+    "msr_decode": (("ret::", "Cijk"), ("vec_step_kernel",)),
 }
+
+
+def _alg_bytes_bwd():
+    """q, k, v, dO read once; dq, dk, dv written once (bf16)."""
+    from workloads import CHUNKWISE_32K as wl
+    return 2 * wl.B * wl.H * wl.L * (2 * wl.dk + 2 * wl.dv) + 2 * wl.B * wl.H * wl.L * (2 * wl.dk + wl.dv)
+
+
+def _alg_bytes_msr():
+    """The gated layer's minimum: X and the five weights read once, Y written once."""
+    from workloads import MSR_LAYER as wl
+    T = wl.B * wl.L
+    return 2 * (2 * T * wl.d_model + wl.d_model * (2 * wl.H * wl.dk + 3 * wl.H * wl.dv))
+
+
+def _alg_bytes_msr_decode():
+    """Per step of 64 sequences: the five weights, the fp32 state read and written,
+    the step's input and output rows."""
+    from workloads import MSR_LAYER as wl
+    B = MSR_DECODE_B
+    return 2 * wl.d_model * (2 * wl.H * wl.dk + 3 * wl.H * wl.dv) + 2 * 4 * B * wl.H * wl.dk * wl.dv + 2 * 2 * B * wl.d_model
 
 
 def pmc_summary(name, fetch_csv, write_csv, command, out_dir=None):
@@ -306,8 +348,8 @@ def pmc_summary(name, fetch_csv, write_csv, command, out_dir=None):
                 per_kernel[r["Kernel_Name"]].append(float(r["Counter_Value"]))
         copy = [v for k, lst in per_kernel.items() if "neg_kernel" in k for v in lst]
         calls = sum(len(lst) for k, lst in per_kernel.items() if any(o in k for o in once))
-        total = sum(sum(lst) for k, lst in per_kernel.items() if incl in k)
-        names = sorted(k for k in per_kernel if incl in k)
+        total = sum(sum(lst) for k, lst in per_kernel.items() if any(i in k for i in incl))
+        names = sorted(k for k in per_kernel if any(i in k for i in incl))
         if not copy or not calls:
             raise SystemExit(f"{path}: no calibration copy or no {once} dispatches")
         copy_kib = sum(copy) / len(copy)
@@ -316,8 +358,9 @@ def pmc_summary(name, fetch_csv, write_csv, command, out_dir=None):
     w_kib, w_copy, _, _ = read(write_csv, "WRITE_SIZE")
     f_fac, w_fac = COPY_BYTES / (f_copy * 1024), COPY_BYTES / (w_copy * 1024)
     hbm = f_kib * 1024 * f_fac + w_kib * 1024 * w_fac
-    alg = {"chunkwise_32k": _alg_bytes_chunkwise(), "decode_step": _alg_bytes_decode(),
-           "parallel_2k": _alg_bytes_parallel()}[name]
+    alg = {"chunkwise_32k": _alg_bytes_chunkwise, "decode_step": _alg_bytes_decode,
+           "parallel_2k": _alg_bytes_parallel, "chunkwise_bwd": _alg_bytes_bwd, "msr_layer": _alg_bytes_msr,
+           "msr_decode": _alg_bytes_msr_decode}[name]()
     out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{name}.txt")
     with open(out, "w") as fh:
         fh.write(f"# HBM traffic per call of {name}: rocprofv3 PMC FETCH_SIZE and WRITE_SIZE (KiB per dispatch),\n"
@@ -437,7 +480,7 @@ def bench_block(steps, warmup):
     ret = T * wl.H * ((C + 1) * (wl.dk + wl.dv) + 4 * wl.dk * wl.dv)
     ffn = 4 * T * wl.d_model * dff
     tf = (gemm + ret + ffn) / per_call / 1e12
-    return {"tokens_per_s": T / per_call, "ms_per_step": per_call * 1e3, "d_ffn": dff,
+    return {"tokens_per_s": T / per_call, "ms_per_step": per_call * 1e3, "d_ffn": dff, **_spread(),
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
                          "kernel": "retnet_block_fwd (LayerNorm, gated layer, residual GEMM, LayerNorm, FFN GEMMs "
@@ -497,34 +540,139 @@ def bench_msr_decode(steps=MSR_DECODE_STEPS):
     bytes_step = weights + 2 * 4 * B * wl.H * wl.dk * wl.dv + 2 * 2 * B * wl.d_model
     achieved = bytes_step / per_step / 1e9
     return {"tokens_per_s": B * steps / t, "ms_per_step": per_step * 1e3, "steps": steps, "batch": B,
+            **{k: v for k, v in _spread().items() if k != "calls_timed"},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": _read_traffic("msr_decode"),
                          "kernel": "msr_layer_step graph replay (fused projection GEMM, vec_step_kernel with "
                                    "GroupNorm and gate, output GEMM, position advance)",
                          "algorithmic_bytes_per_call": bytes_step}}
 
 
-def cpu_baseline(sample_tokens):
-    """The fp64 oracle (chunkwise form, chunk 256) on the first `sample_tokens`
-    tokens of all 8 heads of the long-context workload, timed on host cores."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _omp_threads():
+    """Threads the oracle's OpenMP loops run with: OMP_NUM_THREADS when set (the
+    process's CPU share), else the CPUs this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return int(env) if env.isdigit() and int(env) > 0 else len(os.sched_getaffinity(0))
+
+
+def _set_omp_threads(n):
+    import ctypes
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
+def _recurrent_column_blocks(q, k, v, g, th, ncb):
+    """The oracle's recurrent form with V split into ncb column blocks, each block a
+    head of its own: an output column depends only on the same column of V, so the
+    blocks are independent units for the oracle's OpenMP loop (the rotation of q and
+    k is repeated per block; everything else is the same arithmetic)."""
+    import numpy as np
     import oracle
-    from workloads import CHUNKWISE_32K as wl
-    q, k, v = wl.qkv()
-    n = sample_tokens
-    qs, ks, vs = (oracle.as_f64(t[:, :, :n]) for t in (q, k, v))
-    g, th = wl.gamma(), wl.theta()
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    qq, kk = (np.ascontiguousarray(np.repeat(x, ncb, axis=1)) for x in (q, k))
+    vv = np.ascontiguousarray(v.reshape(B, H, L, ncb, dv // ncb).transpose(0, 1, 3, 2, 4).reshape(B, H * ncb, L, -1))
+    gg = np.repeat(np.asarray(g, dtype=np.float64), ncb)
+
+    def run():
+        return oracle.recurrent(qq, kk, vv, gg, th)
+    return run
+
+
+def cpu_baseline(seconds=10.0):
+    """The fp64 oracle timed on this host's CPUs, after the GPU legs.  Main figure:
+    the recurrent form (the reference form for the long-context workload) over the
+    whole B1 H8 L32768 dk128 dv256 workload, V split into column blocks so that the
+    OpenMP loop has a unit per thread, whole passes until `seconds` have elapsed.
+    Context: one-thread runs of the tiny workload (all three forms), of one (b, h)
+    slice of the parallel workload (the literal double sum) and of the first 4096
+    tokens of the long-context workload (recurrent form)."""
+    import numpy as np
+    import oracle
+    from workloads import CHUNKWISE_32K as wl, PARALLEL_2K, TINY
+    threads = _omp_threads()
+    q, k, v = (oracle.as_f64(t) for t in wl.qkv())
+    g, th = wl.gamma().double().numpy(), wl.theta()
+    ncb = 1
+    while wl.B * wl.H * ncb < threads and wl.dv // (2 * ncb) >= 8:
+        ncb *= 2
+    run = _recurrent_column_blocks(q, k, v, g, th, ncb)
+    _set_omp_threads(threads)
     reps, t0 = 0, time.perf_counter()
-    while True:  # whole passes until about 10 s of CPU work
-        oracle.chunkwise(qs, ks, vs, g, wl.chunk, th)
+    while True:
+        run()
         reps += 1
         dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 50:
+        if dt >= seconds or reps >= 50:
             break
-    return {"value": reps * wl.B * n / dt, "unit": "tokens/s", "cores": min(threads, wl.B * wl.H), "kind": "oracle",
-            "sample": f"fp64 chunkwise oracle (chunk {wl.chunk}) on tokens 0..{n - 1} of all {wl.H} heads of "
-                      f"the L=32768 workload, {reps} passes in {dt:.1f} s; OpenMP over the {wl.B * wl.H} "
-                      f"(b, h) units"}
+    units = wl.B * wl.H * ncb
+    res = {"value": reps * wl.B * wl.L / dt, "unit": "tokens/s", "cores": min(threads, units), "kind": "oracle",
+           "nproc": os.cpu_count(), "cpus_allowed": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
+           "sample": f"fp64 recurrent oracle over the whole chunkwise workload (B1 H8 L32768 dk128 dv256, all 32768 "
+                     f"tokens of all {wl.H} heads), V in {ncb} column blocks: {units} OpenMP units on {threads} "
+                     f"threads, {reps} passes in {dt:.1f} s"}
+    # one-thread context runs
+    _set_omp_threads(1)
+    one = {}
+    try:
+        tq, tk, tv = TINY.qkv()
+        tg, tt = TINY.gamma(), TINY.theta()
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            oracle.parallel(tq, tk, tv, tg, tt)
+            oracle.recurrent(tq, tk, tv, tg, tt)
+            oracle.chunkwise(tq, tk, tv, tg, TINY.chunk, tt)
+            n += 1
+        one["tiny"] = {"tokens_per_s": n * TINY.B * TINY.L / (time.perf_counter() - t0),
+                       "form": "parallel + recurrent + chunkwise, whole workload"}
+        pw = PARALLEL_2K
+        pq, pk, pv = (oracle.as_f64(x[:1, :1]) for x in pw.qkv())
+        t0 = time.perf_counter()
+        oracle.parallel(pq, pk, pv, pw.gamma()[:1], pw.theta())
+        dt1 = time.perf_counter() - t0
+        one["parallel"] = {"tokens_per_s": pw.L / pw.H / dt1, "seconds": dt1,
+                           "form": "literal double sum on one (b, h) slice (a token counts once over its 8 heads)"}
+        m = 4096
+        t0 = time.perf_counter()
+        oracle.recurrent(q[:, :, :m], k[:, :, :m], v[:, :, :m], g, th)
+        dt1 = time.perf_counter() - t0
+        one["chunkwise"] = {"tokens_per_s": wl.B * m / dt1, "seconds": dt1,
+                            "form": f"recurrent form on tokens 0..{m - 1} of all {wl.H} heads"}
+    finally:
+        _set_omp_threads(threads)
+    res["one_thread"] = one
+    return res
+
+
+def probe_peaks():
+    """Rates this GPU attains beside the spec peaks: a plain HBM copy (torch.neg over
+    1 GiB of bf16: 1 GiB read + 1 GiB written) and a large dense bf16 GEMM
+    (torch.matmul, 8192 x 8192 x 8192, the vendor library)."""
+    import torch
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    t = _time_calls(lambda: torch.neg(src, out=dst), 20, 3)
+    copy = 2 * 2 * n * 20 / t / 1e9
+    del src, dst
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty_like(a)
+    t = _time_calls(lambda: torch.matmul(a, b, out=c), 20, 3)
+    gemm = 2 * 8192 ** 3 * 20 / t / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": copy, "bf16_gemm_tflops": gemm,
+            "what": "torch.neg over 1 GiB bf16 (bytes read + written); torch.matmul 8192^3 bf16"}
 
 
 def main():
@@ -534,7 +682,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="headline chunkwise workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time of the CPU oracle's main figure")
     ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "msr", "msr_decode", "sweep", "bwd",
                                        "block"],
                     help="run one workload and print its figures (for profiling runs)")
@@ -591,6 +739,7 @@ def main():
                    "heads": CHUNKWISE_32K.H, "dk": CHUNKWISE_32K.dk, "dv": CHUNKWISE_32K.dv,
                    "chunk": CHUNKWISE_32K.chunk},
         "roofline": ch["roofline"], "chunkwise_mfma": ch["mfma"],
+        "median_ms_per_step": ch.get("median_ms"), "min_ms_per_step": ch.get("min_ms"),
     }
     if not (args.no_extra or args.only):
         _log("decode B128 H16, 1024 steps")
@@ -607,9 +756,17 @@ def main():
         line["msr_decode"] = bench_msr_decode()
         _log("chunk-size sweep")
         line["chunk_sweep"] = bench_chunk_sweep(max(5, args.steps // 2), args.warmup)
+    if not args.only:
+        _log("probe peaks (HBM copy, bf16 GEMM)")
+        pk = line["probe_peaks"] = probe_peaks()
+        for leg in [line] + [v for v in line.values() if isinstance(v, dict) and "roofline" in v]:
+            r = leg["roofline"]
+            att = pk["hbm_copy_gbs"] if r["bound"] == "hbm" else pk["bf16_gemm_tflops"]
+            r["attainable"] = att
+            r["frac_of_attainable"] = r["achieved"] / att
     if not (args.no_cpu or args.only):
-        _log(f"cpu baseline ({args.cpu_tokens} tokens)")
-        line["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+        _log("cpu baseline")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -97,3 +97,21 @@ def test_util_summary_normalisation(tmp_path):
     assert abs(float(vals["lds_busy"]) - 0.5) < 1e-3
     assert abs(float(vals["lds_bank_conflict"]) - 0.1) < 1e-3
     assert abs(float(vals["lds_wait"]) - 0.1) < 1e-3
+
+
+def test_layer_legs_count_library_gemms(tmp_path):
+    """The gated layer's legs sum this library's kernels and the hipBLASLt GEMMs of a
+    call (Cijk...), counting calls by a kernel that runs once per call."""
+    copy_kib = bench.COPY_BYTES / 1024
+    gemm = "Custom_Cijk_Alik_Bljk_BBS_BH_Bias_HA_S_SAV_NTD_SK3_UserArgs_MT256x256x64_MI16x16x1_shortname0_gfx950"
+    scan = "ret::seg_scan_t_kernel(ret::RetArgs, ret::TaskGeom, float const*, unsigned short*, float const*, flo"
+    out = "void ret::qblock_kernel<256, 512, false, false>(ret::RetArgs, ret::TaskGeom, unsigned short const*)"
+    fetch = [("void at::native::neg_kernel", copy_kib / 2), ("void at::native::fill_kernel", 5000.0)]
+    write = [("void at::native::neg_kernel", copy_kib), ("void at::native::fill_kernel", 5000.0)]
+    for _ in range(4):
+        fetch += [(gemm, 400.0), (scan, 50.0), (out, 300.0), (gemm, 100.0)]
+        write += [(gemm, 200.0), (scan, 25.0), (out, 100.0), (gemm, 60.0)]
+    vals = _summary(tmp_path, "msr_layer", fetch, write)
+    assert float(vals["fetch_kib_per_call"]) == 850.0
+    assert float(vals["write_kib_per_call"]) == 385.0
+    assert int(vals["algorithmic_bytes_per_call"]) == bench._alg_bytes_msr()
