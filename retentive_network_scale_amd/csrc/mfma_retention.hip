@@ -755,6 +755,65 @@ __device__ __forceinline__ u32x4 ld_op_trs(const uint16_t *Vb, int k0, int m0, i
   return u32x4{l.x, l.y, h.x, h.y};
 }
 
+// Rotated key tiles by LDS-DMA: 64 token rows of DK bf16, unpadded, the 16-byte
+// chunk c of row r stored at chunk c ^ (r & 7).  The score operand of lane
+// (g, l16) is 8 consecutive elements (chunk 4ks + g) of row r0 + l16: each run
+// of 8 lanes then reads 8 different chunk slots of rows with equal bank
+// offsets, i.e. all 32 banks once (DK*2 is a multiple of 128 bytes).  Wave
+// instruction J writes LDS bytes [1024 J, 1024 J + 1024), lane l 16 of them;
+// rows at or past `valid` read as zero.
+template <int DK>
+__device__ __forceinline__ void k_dma(uint16_t *Ks, const uint16_t *src, long long sn, int valid) {
+  constexpr int RBYTES = DK * 2, NJ = BT * RBYTES / 1024 / (NT / 64);  // instructions per wave
+  static_assert(BT * RBYTES % (1024 * (NT / 64)) == 0 && DK >= 64, "whole instructions per wave, 8 chunks a row");
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int nbytes = valid > 0 ? (int)((long long)valid * sn * 2) : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nbytes, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int J = w * NJ + j, off = J * 1024 + 16 * l;
+    const int row = off / RBYTES, c = ((off % RBYTES) >> 4) ^ (row & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(Ks + J * 512), 16,
+                                             (int)(row * sn * 2) + 16 * c, 0, 0, 0);
+  }
+}
+
+// Elements [8c, 8c + 8) of row r of a key tile in that layout.
+template <int DK>
+__device__ __forceinline__ u32x4 ld_k8(const uint16_t *Ks, int r, int c) {
+  return *(const u32x4 *)(Ks + r * DK + 8 * (c ^ (r & 7)));
+}
+
+// The rotated keys of a call, once, for the query-block kernels:
+// kt[((b H + h) L + n) DK + j] = bf16 of k[b, h, n, :] with pair i = (2i, 2i+1)
+// turned by the angle (pos0 + n) theta_i ("Retentive Network" paper summary,
+// Sec. 2.1: the e^(i n theta) factor of Q and K).  One thread per 8 elements;
+// each token's angle is reduced in fp64 from its own position.
+template <int DK>
+__global__ __launch_bounds__(256) void rotate_keys_kernel(RetArgs a, uint16_t *kt) {
+  constexpr int C8 = DK / 8;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = idx / C8;  // (b H + h) L + n
+  if (row >= (long long)a.B * a.H * a.L) return;
+  const int c8 = (int)(idx % C8), n = (int)(row % a.L);
+  const long long bh = row / a.L;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  const uint16_t *src = (const uint16_t *)a.k + (long long)b * a.q_sb + (long long)h * a.q_sh + (long long)n * a.q_sn;
+  // streamed: the input keys are not read again by this call, and caching them
+  // would evict what the retention kernel reads next
+  const u32x4 x = __builtin_nontemporal_load((const u32x4 *)(src + 8 * c8));
+  const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float re = __uint_as_float(wv[e] << 16), im = __uint_as_float(wv[e] & 0xffff0000u);
+    const float A = base_rev(a.pos0 + n, a.theta[4 * c8 + e]);
+    const float c = __builtin_amdgcn_cosf(A), sn = __builtin_amdgcn_sinf(A);
+    o[e] = pack_bf2(re * c - im * sn, re * sn + im * c);
+  }
+  *(u32x4 *)(kt + row * DK + 8 * c8) = u32x4{o[0], o[1], o[2], o[3]};
+}
+
 // Waits for this wave's outstanding vector-memory operations, LDS-DMA loads
 // included (s_waitcnt vmcnt(0)).  A DMA-filled tile is read by other waves, so
 // every wave calls this before the barrier that publishes the tile.
@@ -782,8 +841,14 @@ __device__ __forceinline__ void lds_barrier() {
 // magnify absolute score errors by ~1/sqrt(eps).
 // The global loads of the next key block are issued right after the current
 // one is committed to LDS, so they are in flight during the MFMA work.
-template <int DK, int DV, bool PAR, bool SPLIT>
-__global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, const uint16_t *SinT) {
+// KPRE (plain scores only): the keys arrive rotated -- from kt ([B*H][L][DK],
+// rotate_keys_kernel), or straight from k when there is no rotation (kt null) --
+// and go to LDS by DMA, no register pass: the next block's DMA is issued once
+// the scores are done with the current one and lands during the P.V products.
+template <int DK, int DV, bool PAR, bool SPLIT, bool KPRE = false>
+__global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, const uint16_t *SinT,
+                                                    const uint16_t *kt = nullptr) {
+  static_assert(!(KPRE && SPLIT), "pre-rotated keys carry no lo part");
   using T = Tile<DK, DV>;
   constexpr int LDQ = T::LDQ, RW = T::RW, RB = T::RB, KS = T::KS;
   // The query block is staged through Ks / KsL (free until the key loop starts).
@@ -795,7 +860,10 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   __shared__ float2 step_s[DK / 2];
   __shared__ float red[8][BT];
   __shared__ float dt[DT_SZ];
-  uint16_t *const Qs = Ks;
+  // With keys by DMA the query tile is staged in the V tile's space where it
+  // fits, so that the first key block can load from the start.
+  constexpr bool QV = KPRE && DV >= DK + 4;
+  uint16_t *const Qs = QV ? Vb : Ks;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int task = xcd_task(blockIdx.x, geo.ntasks);
@@ -825,9 +893,13 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   if (rot) fill_rot_tables(a, theta_s, step_s, DK / 2);
   fill_decay_table(dt, lg, NT);
 
+  // key rows of this (b, h): the rotated copy, else the input
+  const uint16_t *ksrc = kt ? kt + (long long)bh * a.L * DK : k;
+  const long long ksn = kt ? DK : a.q_sn;
   TileIO<DK> qio, kio;
+  if constexpr (QV) k_dma<DK>(Ks, ksrc + (long long)c0 * ksn, ksn, min(BT, Cc));
   qio.fetch(q + (long long)q0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - q0));
-  kio.fetch(k + (long long)c0 * a.q_sn, a.q_sn, min(BT, Cc));
+  if constexpr (!KPRE) kio.fetch(k + (long long)c0 * a.q_sn, a.q_sn, min(BT, Cc));
   __syncthreads();
   qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, step_s, Qs, LDQ, KsL, nullptr, false, 0.f, 0);
   __syncthreads();
@@ -838,14 +910,6 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   constexpr int QW = SPLIT ? 1 : 2, KW = 2 / QW;
   const int qp = w % (4 / QW), kq = w / (4 / QW);
   const int qrow0 = 16 * QW * qp, krow0 = 16 * KW * kq;
-  u32x4 qreg[QW][KS], qlo[QW][SPLIT ? KS : 1];
-#pragma unroll
-  for (int qq = 0; qq < QW; ++qq)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qreg[qq][ks] = ld_op(Qs + (qrow0 + 16 * qq + l16) * LDQ, 32 * ks, g);
-      if constexpr (SPLIT) qlo[qq][ks] = ld_op(KsL + (qrow0 + 16 * qq + l16) * LDQ, 32 * ks, g);
-    }
   // O^T accumulators: ot[rb][qb4][i] = O^T[w*RW+16rb+4g+i][16qb4+l16]
   f32x4 ot[RB][4];
 #pragma unroll
@@ -882,15 +946,41 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
       for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] *= xi;
     }
   }
+  // the query operands of the scores (read after the cross term: fewer live registers there)
+  u32x4 qreg[QW][KS], qlo[QW][SPLIT ? KS : 1];
+#pragma unroll
+  for (int qq = 0; qq < QW; ++qq)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (KPRE) {  // k-step elements 8g..8g+7, as ld_k8 gives the keys
+        const uint16_t *qr = Qs + (qrow0 + 16 * qq + l16) * LDQ + 32 * ks + 8 * g;
+        const u32x2 lo = *(const u32x2 *)qr, hi = *(const u32x2 *)(qr + 4);
+        qreg[qq][ks] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      } else {
+        qreg[qq][ks] = ld_op(Qs + (qrow0 + 16 * qq + l16) * LDQ, 32 * ks, g);
+      }
+      if constexpr (SPLIT) qlo[qq][ks] = ld_op(KsL + (qrow0 + 16 * qq + l16) * LDQ, 32 * ks, g);
+    }
+  if constexpr (KPRE && !QV) {  // the query tile (Qs = Ks) is read: the first key block
+    __syncthreads();
+    k_dma<DK>(Ks, ksrc + (long long)c0 * ksn, ksn, min(BT, Cc));
+  }
   for (int kb = 0; kb <= qb; ++kb) {
     const int k0 = c0 + kb * BT;
     const int delta = qb - kb;
     const float gdel = delta ? dpow(lg, 64 * (delta - 1)) : 1.0f;
-    __syncthreads();
-    // this visit's V tile streams into LDS during the key commit and the scores
-    v_dma<DV>(Vb, v + (long long)k0 * a.v_sn, a.v_sn, min(BT, c0 + Cc - k0));
-    kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, step_s, Ks, LDQ, KsL, nullptr, false, 0.f, 0);
-    lds_barrier();  // the keys; the V tile stays in flight
+    if constexpr (KPRE) {
+      wait_vmem();  // this wave's part of the key tile; the barrier publishes all of it
+      __syncthreads();
+      v_dma<DV>(Vb, v + (long long)k0 * a.v_sn, a.v_sn, min(BT, c0 + Cc - k0));
+    } else {
+      __syncthreads();
+      // this visit's V tile streams into LDS during the key commit and the scores
+      v_dma<DV>(Vb, v + (long long)k0 * a.v_sn, a.v_sn, min(BT, c0 + Cc - k0));
+      kio.template commit<true, false, SPLIT>(rot, a.pos0 + k0, theta_s, step_s, Ks, LDQ, KsL, nullptr, false, 0.f,
+                                              0);
+      lds_barrier();  // the keys; the V tile stays in flight
+    }
     // scores S^T[key][query] for the wave's keys and queries; decay, mask, -> Ps
 #pragma unroll
     for (int kb = 0; kb < KW; ++kb) {
@@ -899,7 +989,8 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
       for (int qq = 0; qq < QW; ++qq) sc[qq] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 ak = ld_op(Ks + (krow0 + 16 * kb + l16) * LDQ, 32 * ks, g);
+        const u32x4 ak = KPRE ? ld_k8<DK>(Ks, krow0 + 16 * kb + l16, 4 * ks + g)
+                              : ld_op(Ks + (krow0 + 16 * kb + l16) * LDQ, 32 * ks, g);
         u32x4 akl;
         if constexpr (SPLIT) akl = ld_op(KsL + (krow0 + 16 * kb + l16) * LDQ, 32 * ks, g);
 #pragma unroll
@@ -926,7 +1017,10 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
     __syncthreads();
     if (kb < qb) {  // the next visit's keys, in flight during the P.V products
       const int n0 = k0 + BT;
-      kio.fetch(k + (long long)n0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - n0));
+      if constexpr (KPRE)
+        k_dma<DK>(Ks, ksrc + (long long)n0 * ksn, ksn, min(BT, c0 + Cc - n0));
+      else
+        kio.fetch(k + (long long)n0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - n0));
     }
     // O^T += V^T P^T
 #pragma unroll
@@ -1543,6 +1637,35 @@ static bool split_all_blocks(const RetArgs &a) {
   return false;
 }
 
+// Stream-ordered scratch for the parallel form's rotated keys (that call takes
+// no workspace).  The device's default memory pool is told once to keep what is
+// freed (release threshold raised), so repeated calls reuse the same memory
+// instead of mapping it again.
+static hipError_t scratch_alloc(void **p, size_t bytes, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    static std::mutex mu;
+    static std::map<int, bool> kept;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!kept[dev]) {
+      hipMemPool_t pool;
+      if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+        uint64_t thr = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+      }
+      (void)hipGetLastError();
+      kept[dev] = true;
+    }
+  }
+  return hipMallocAsync(p, bytes, st);
+}
+
+// The parallel form's plain-score launches take their keys by DMA, rotated once
+// into stream-ordered scratch first; the chunkwise query-block launches (short
+// tasks of at most chunk/64 visits, measured slower that way) rotate each key
+// block as they stage it.
 template <int DK, int DV>
 static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const uint16_t *sinT, hipStream_t st,
                               bool fork) {
@@ -1552,12 +1675,21 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
   const dim3 grid(xcd_grid(geo.ntasks));
   if (split_all_blocks(a)) {
     if (par)
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid, dim3(NT), 0, st, a, geo, sinT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid, dim3(NT), 0, st, a, geo, sinT, nullptr);
     else
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid, dim3(NT), 0, st, a, geo, sinT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid, dim3(NT), 0, st, a, geo, sinT, nullptr);
     return hipGetLastError();
   }
-  if (a.use_gn && a.use_theta) {
+  if (a.in_rev) return hipErrorNotSupported;  // reversed inputs: the segment kernels only
+  uint16_t *kt = nullptr;
+  if (par && a.use_theta) {
+    const long long nth = (long long)a.B * a.H * a.L * (DK / 8);
+    const hipError_t e = scratch_alloc((void **)&kt, (size_t)nth * 16, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(rotate_keys_kernel<DK>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st, a, kt);
+  }
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && a.use_gn && a.use_theta) {
     // Under GroupNorm a row whose output variance is near eps is divided by
     // about sqrt(eps), which magnifies the rounding of the rotated q and k to
     // bf16: the first query block of a sequence (the rows that sum the fewest
@@ -1582,25 +1714,30 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
         (void)hipGetLastError();
     }
     if (par) {
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid1, dim3(NT), 0, st1, a, g1, sinT);
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, g2, sinT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, true>), grid1, dim3(NT), 0, st1, a, g1, sinT, nullptr);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false, true>), grid, dim3(NT), 0, st, a, g2, sinT, kt);
     } else {
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid1, dim3(NT), 0, st1, a, g1, sinT);
-      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, g2, sinT);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, true>), grid1, dim3(NT), 0, st1, a, g1, sinT, nullptr);
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, g2, sinT, nullptr);
     }
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (st1 != st) {
       const hipError_t ej = hipEventRecord(ss->join, st1) == hipSuccess ? hipStreamWaitEvent(st, ss->join, 0)
                                                                          : hipGetLastError();
       if (e == hipSuccess) e = ej;
     }
-    return e;
-  } else if (par) {
-    hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, sinT);
-  } else {
-    hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, sinT);
+  } else if (e == hipSuccess) {
+    if (par)
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, true, false, true>), grid, dim3(NT), 0, st, a, geo, sinT, kt);
+    else
+      hipLaunchKernelGGL((qblock_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, sinT, nullptr);
+    e = hipGetLastError();
   }
-  return hipGetLastError();
+  if (kt) {
+    const hipError_t ef = hipFreeAsync(kt, st);
+    if (e == hipSuccess) e = ef;
+  }
+  return e;
 }
 
 template <int DK, int DV>
