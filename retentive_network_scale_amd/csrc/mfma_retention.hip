@@ -1192,12 +1192,12 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) st[dkb][rb] *= gc;
       }
-      // key blocks in zigzag order: forward for even query blocks, backward for
-      // odd ones, so the V blocks of one block's last visits are the next
-      // block's first and still in L2 (the sums do not depend on the order)
-      const bool fwd = (qb & 1) == 0;
+      // key blocks qb-1, qb-2, ..., 0, then the diagonal block qb: a block's last
+      // visit and the next block's first visit (inside a chunk) take the same
+      // key block, whose tiles are then still in registers and not fetched
+      // again (the sums do not depend on the order)
       for (int vi = 0; vi <= qb; ++vi) {
-        const int kb = fwd ? vi : qb - vi;
+        const int kb = vi < qb ? qb - 1 - vi : qb;
         const bool last_visit = vi == qb;
         const int k0 = c0 + kb * BT;
         const bool upd = carry && last_qb;
@@ -1228,15 +1228,16 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
         // of the next query block (of this chunk, or query block 0 of the next
         // chunk).  Its loads are issued in two parts -- K before the scores, V
         // before PV -- so the memory system absorbs them while the MFMAs run.
-        int nk0 = k0 + (fwd ? BT : -BT), nend = c0 + Cc;
-        if (last_visit) {
-          const int nc0 = last_qb ? c0 + Cc : c0, nqb = last_qb ? 0 : qb + 1;
-          nk0 = nc0 + ((nqb & 1) == 0 ? 0 : nqb * BT);
-          nend = min(a.L, nc0 + a.chunk);
+        int nk0 = c0 + (vi + 1 < qb ? qb - 2 - vi : qb) * BT, nend = c0 + Cc;
+        if (last_visit && last_qb) {  // key block 0 of the next chunk
+          nk0 = c0 + Cc;
+          nend = min(a.L, nk0 + a.chunk);
         }
         const bool has_next = nk0 < t_hi;
+        const bool same_tile = last_visit && !last_qb;  // its raw tiles are still in registers
         if constexpr (!RES)
-          if (has_next) kio.fetch(tile_src(k, nk0, min(BT, nend - nk0), a.q_sn, a), a.q_sn, min(BT, nend - nk0), a.in_rev);
+          if (has_next && !same_tile)
+            kio.fetch(tile_src(k, nk0, min(BT, nend - nk0), a.q_sn, a), a.q_sn, min(BT, nend - nk0), a.in_rev);
         // at the last visit: the next block's query tile (and resident key
         // tile), committed at the next block boundary.  Issued this late so the
         // registers are free during the earlier visits.
@@ -1266,7 +1267,8 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
           for (int i = 0; i < 4; ++i) p[i] = sc[i] * (gdel * dt[dp - i]);
           *(u32x2 *)(Ps + (16 * qblk + l16) * LDT + 32 * kh + 16 * kb16 + 4 * g) = pack4(p[0], p[1], p[2], p[3]);
         }
-        if (has_next) vio.fetch(tile_src(v, nk0, min(BT, nend - nk0), a.v_sn, a), a.v_sn, min(BT, nend - nk0), a.in_rev);
+        if (has_next && !same_tile)
+          vio.fetch(tile_src(v, nk0, min(BT, nend - nk0), a.v_sn, a), a.v_sn, min(BT, nend - nk0), a.in_rev);
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
