@@ -89,7 +89,7 @@ ret_status_t retention_fail_(ret_status_t s, const char *msg);
 static ret_status_t launch_fail(hipError_t e) {
   if (e == hipErrorNotSupported)
     return retention_fail_(RET_ERR_UNSUPPORTED, "hipBLASLt offers no algorithm for one of the GEMM shapes");
-  return launch_fail(e);
+  return retention_fail_(RET_ERR_HIP, hipGetErrorString(e));
 }
 
 // The layer on validated arguments: y = MSR(x) (+ residual, same layout as y).

@@ -222,3 +222,34 @@ def test_position_and_size_limits():
     r = lib.msr_layer_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, 1, 8, 256, 2, 128, 256, 8, g, None, 2 ** 31 - 7,
                           1e-5, None, 0, None)
     assert r == INVALID
+
+
+_STEP_NO_DEVICE = r"""
+import ctypes, sys
+import retentive_network_scale_amd as rn
+L = rn.lib()
+g = (ctypes.c_float * 2)(0.9, 0.95)
+need = L.msr_layer_step_workspace_bytes(4, 256, 2, 64, 128)
+P = ctypes.c_void_p
+# non-overlapping stand-in addresses; the host never dereferences them and the
+# first HIP call fails for want of a device
+r = L.msr_layer_step(P(0x100000), P(0x100000), P(0x100000), P(0x100000), P(0x100000), P(0x100000),
+                     P(0x200000), P(0x300000), P(0x400000), 1, 4, 256, 2, 64, 128, g, None, 1e-5,
+                     P(0x10000000), need, None)
+msg = L.retention_last_error()
+print(r, msg)
+sys.exit(0 if r == 4 and b"device" in msg else 1)
+"""
+
+
+def test_launch_error_is_reported_not_recursed():
+    """A HIP failure inside the gated layer's launch sequence comes back as the
+    HIP-error status with the runtime's message."""
+    import subprocess
+    import sys
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("needs a host without a usable GPU: the call would launch on stand-in pointers")
+    r = subprocess.run([sys.executable, "-c", _STEP_NO_DEVICE], cwd=ROOT, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout[-500:], r.stderr[-500:])
