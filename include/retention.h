@@ -228,7 +228,10 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
  *         step, so a captured call can be replayed without host updates
  * UNSUPPORTED unless d_model, H*dk and H*dv are multiples of 128, dk and dv are
  * multiples of 8 and dv <= 1024.  y, state, x and the workspace must not overlap.
- * The projections run through hipBLASLt as in msr_layer_fwd.
+ * The projections run through hipBLASLt as in msr_layer_fwd but are kept in
+ * fp32 (a (token, head) row whose retention output nearly cancels is divided by
+ * its small deviation in GroupNorm, which would magnify a bf16 rounding of q and
+ * k); W_O takes the bf16 gated heads.
  */
 size_t msr_layer_step_workspace_bytes(int B, int d_model, int H, int dk, int dv);
 ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, const void *w_v,

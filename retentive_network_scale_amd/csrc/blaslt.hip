@@ -6,8 +6,9 @@
 // is used for them; everything specific to retention runs in this library's own
 // kernels.
 //
-//   C[t][n] = sum_k X[t][k] W[n][k] (+ R[t][n])   (row-major, bf16 in and out,
-//                                                  fp32 accumulate; R optional)
+//   C[t][n] = sum_k X[t][k] W[n][k] (+ R[t][n])   (row-major, bf16 in, bf16 or
+//                                                  fp32 out, fp32 accumulate;
+//                                                  R optional, bf16 out only)
 //
 // In hipBLASLt's column-major terms this is C^T (N x T, ld ldc) = W (N x K) * X^T
 // (K x T), with W given as its stored K x N column-major transpose: a "TN" product.
@@ -34,10 +35,11 @@ struct Plan {
 
 std::mutex g_mu;
 std::map<int, hipblasLtHandle_t> g_handles;
-std::map<std::tuple<int, int, int, int, int, size_t>, Plan> g_plans;
+std::map<std::tuple<int, int, int, int, int, size_t, bool>, Plan> g_plans;
 
 // Builds (or finds) the plan for this device and shape; nullptr when hipBLASLt has no algorithm for it.
-const Plan *get_plan(int dev, hipblasLtHandle_t *handle, int T, int N, int K, int ldc, size_t ws_bytes) {
+const Plan *get_plan(int dev, hipblasLtHandle_t *handle, int T, int N, int K, int ldc, size_t ws_bytes,
+                     bool out_f32) {
   std::lock_guard<std::mutex> lock(g_mu);
   auto hit = g_handles.find(dev);
   if (hit == g_handles.end()) {
@@ -46,7 +48,7 @@ const Plan *get_plan(int dev, hipblasLtHandle_t *handle, int T, int N, int K, in
     hit = g_handles.emplace(dev, h).first;
   }
   *handle = hit->second;
-  const auto key = std::make_tuple(dev, T, N, K, ldc, ws_bytes);
+  const auto key = std::make_tuple(dev, T, N, K, ldc, ws_bytes, out_f32);
   auto pit = g_plans.find(key);
   if (pit != g_plans.end()) return pit->second.ok ? &pit->second : nullptr;
   Plan p;
@@ -58,7 +60,8 @@ const Plan *get_plan(int dev, hipblasLtHandle_t *handle, int T, int N, int K, in
                  HIPBLAS_STATUS_SUCCESS;
   ok = ok && hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS;
   ok = ok && hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, K, T, K) == HIPBLAS_STATUS_SUCCESS;
-  ok = ok && hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_16BF, N, T, ldc) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&p.lc, out_f32 ? HIP_R_32F : HIP_R_16BF, N, T, ldc) ==
+                 HIPBLAS_STATUS_SUCCESS;
   if (ok) {
     hipblasLtMatmulPreference_t pref = nullptr;
     const uint64_t max_ws = ws_bytes;
@@ -83,17 +86,19 @@ const Plan *get_plan(int dev, hipblasLtHandle_t *handle, int T, int N, int K, in
 
 }  // namespace
 
-hipError_t blaslt_gemm_nt(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, int N, int K, int ldc,
-                          void *ws, size_t ws_bytes, hipStream_t st, const uint16_t *R) {
+hipError_t blaslt_gemm_nt(const uint16_t *X, const uint16_t *W, void *C, int T, int N, int K, int ldc, void *ws,
+                          size_t ws_bytes, hipStream_t st, const uint16_t *R, bool out_f32) {
+  if (R && out_f32) return hipErrorInvalidValue;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   hipblasLtHandle_t handle = nullptr;
-  const Plan *p = get_plan(dev, &handle, T, N, K, ldc, ws_bytes);
+  const Plan *p = get_plan(dev, &handle, T, N, K, ldc, ws_bytes, out_f32);
   if (!p) return hipErrorNotSupported;
   const float alpha = 1.0f, beta = R ? 1.0f : 0.0f;
-  const hipblasStatus_t s = hipblasLtMatmul(handle, p->desc, &alpha, W, p->la, X, p->lb, &beta, R ? R : C, p->lc,
-                                            C, p->lc, &p->algo, p->ws ? ws : nullptr, p->ws, st);
+  const void *Cin = R ? (const void *)R : (const void *)C;
+  const hipblasStatus_t s = hipblasLtMatmul(handle, p->desc, &alpha, W, p->la, X, p->lb, &beta, Cin, p->lc, C,
+                                            p->lc, &p->algo, p->ws ? ws : nullptr, p->ws, st);
   return s == HIPBLAS_STATUS_SUCCESS ? hipSuccess : hipErrorLaunchFailure;
 }
 

@@ -17,7 +17,8 @@ constexpr int kMaxPairs = RETENTION_MAX_DK / 2;
 struct RetArgs {
   const void *q, *k, *v;
   void *o;
-  const uint16_t *gate;  // optional bf16 multiplier applied after GroupNorm (gated layer)
+  const uint16_t *gate;  // optional multiplier applied after GroupNorm (gated layer); bf16, or
+                         // fp32 on the vector kernels when the inputs are fp32
   int gate_swish;        // the multiplier is swish(gate) = gate / (1 + exp(-gate)) instead of gate
   // Output transforms of the MFMA epilogue (used by the backward): out_rev stores
   // row n at L-1-n; out_rot multiplies output pair i of a row whose source token

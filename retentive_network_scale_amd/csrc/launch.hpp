@@ -48,8 +48,9 @@ hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &plan, void *
 // (+ R[t][n] when R is given, same layout as C) for t < T, n < N, row-major with
 // row stride ldc.  hipErrorNotSupported when hipBLASLt has no algorithm for the
 // shape within ws_bytes of workspace.
-hipError_t blaslt_gemm_nt(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, int N, int K, int ldc,
-                          void *ws, size_t ws_bytes, hipStream_t st, const uint16_t *R = nullptr);
+// out_f32: C is fp32 (no residual then).
+hipError_t blaslt_gemm_nt(const uint16_t *X, const uint16_t *W, void *C, int T, int N, int K, int ldc, void *ws,
+                          size_t ws_bytes, hipStream_t st, const uint16_t *R = nullptr, bool out_f32 = false);
 
 // Row-wise bf16 passes of the residual block (block.hip): LayerNorm without
 // affine (y may alias x) and exact gelu in place.

@@ -47,24 +47,29 @@ MsrLayout msr_layout(int B, int L, int H, int dk, int dv, int chunk) {
   return m;
 }
 
-// C[t][n] = sum_k X[t][k] W[n][k] (+ R[t][n]) (row stride ldc) through hipBLASLt;
-// hipErrorNotSupported when hipBLASLt offers no algorithm for the shape.
-hipError_t plain_gemm(const uint16_t *X, const uint16_t *W, uint16_t *C, int T, int N, int K, int ldc, void *blas_ws,
-                      hipStream_t st, const uint16_t *R = nullptr) {
-  return blaslt_gemm_nt(X, W, C, T, N, K, ldc, blas_ws, BLAS_WS, st, R);
+// C[t][n] = sum_k X[t][k] W[n][k] (+ R[t][n]) (row stride ldc; bf16, or fp32 when
+// out_f32) through hipBLASLt; hipErrorNotSupported when hipBLASLt offers no
+// algorithm for the shape.
+hipError_t plain_gemm(const uint16_t *X, const uint16_t *W, void *C, int T, int N, int K, int ldc, void *blas_ws,
+                      hipStream_t st, const uint16_t *R = nullptr, bool out_f32 = false) {
+  return blaslt_gemm_nt(X, W, C, T, N, K, ldc, blas_ws, BLAS_WS, st, R, out_f32);
 }
 
-// P[T][NP] = X [W_Q|W_K|W_V|W_G]^T.  When the four weights sit back to back in
-// memory (one [2 H dk + 2 H dv][K] matrix, rows in that order) this is a single
-// GEMM over all NP columns; otherwise one GEMM per weight.
-hipError_t projections(const uint16_t *X, const void *w_q, const void *w_k, const void *w_v, const void *w_g,
-                       uint16_t *P, int T, int K, int H, int dk, int dv, void *blas_ws, hipStream_t st) {
+// P[T][NP] = X [W_Q|W_K|W_V|W_G]^T (fp32 for a decode step, else bf16), plain
+// hipBLASLt GEMMs.  When the
+// four weights sit back to back in memory (one [2 H dk + 2 H dv][K] matrix, rows
+// in that order) this is a single GEMM over all NP columns; otherwise one GEMM
+// per weight.
+hipError_t projections(bool step, const uint16_t *X, const void *w_q, const void *w_k, const void *w_v,
+                       const void *w_g, void *P, int T, int K, int H, int dk, int dv, void *blas_ws,
+                       hipStream_t st) {
+  const size_t esz = step ? 4 : 2;
   const long long NP = 2LL * H * dk + 2LL * H * dv;
   const size_t qk_bytes = (size_t)H * dk * K * 2, vg_bytes = (size_t)H * dv * K * 2;
   const char *q = (const char *)w_q;
   if ((const char *)w_k == q + qk_bytes && (const char *)w_v == q + 2 * qk_bytes &&
       (const char *)w_g == q + 2 * qk_bytes + vg_bytes)
-    return plain_gemm(X, (const uint16_t *)w_q, P, T, (int)NP, K, (int)NP, blas_ws, st);
+    return plain_gemm(X, (const uint16_t *)w_q, P, T, (int)NP, K, (int)NP, blas_ws, st, nullptr, step);
   const struct {
     const void *w;
     long long col;
@@ -72,7 +77,8 @@ hipError_t projections(const uint16_t *X, const void *w_q, const void *w_k, cons
   } proj_w[4] = {{w_q, 0, H * dk}, {w_k, (long long)H * dk, H * dk}, {w_v, 2LL * H * dk, H * dv},
                  {w_g, 2LL * H * dk + (long long)H * dv, H * dv}};
   for (const auto &pw : proj_w) {
-    hipError_t e = plain_gemm(X, (const uint16_t *)pw.w, P + pw.col, T, pw.n, K, (int)NP, blas_ws, st);
+    hipError_t e = plain_gemm(X, (const uint16_t *)pw.w, (char *)P + pw.col * esz, T, pw.n, K, (int)NP, blas_ws,
+                              st, nullptr, step);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -104,7 +110,7 @@ static ret_status_t msr_forward(const void *x, const void *w_q, const void *w_k,
 
   // 1. projections into P
   {
-    hipError_t e = projections((const uint16_t *)x, w_q, w_k, w_v, w_g, proj, (int)T, d_model, H, dk, dv,
+    hipError_t e = projections(false, (const uint16_t *)x, w_q, w_k, w_v, w_g, proj, (int)T, d_model, H, dk, dv,
                                ws + m.blas, st);
     if (e != hipSuccess) return launch_fail(e);
   }
@@ -211,11 +217,11 @@ ret_status_t msr_layer_fwd(const void *x, const void *w_q, const void *w_k, cons
 size_t msr_layer_step_workspace_bytes(int B, int d_model, int H, int dk, int dv) {
   if (B <= 0 || d_model <= 0 || H <= 0 || dk <= 0 || dv <= 0) return 0;
   const size_t NP = 2 * (size_t)H * dk + 2 * (size_t)H * dv;
-  return align256((size_t)B * NP * 2) + align256((size_t)B * H * dv * 2) + BLAS_WS;
+  return align256((size_t)B * NP * 4) + align256((size_t)B * H * dv * 2) + BLAS_WS;
 }
 
 // One decode step of the gated layer for B sequences (one token each):
-//   P = x [W_Q|W_K|W_V|W_G]^T (plain GEMMs), the recurrent retention step of every
+//   P = x [W_Q|W_K|W_V|W_G]^T (plain GEMMs, fp32 out), the recurrent retention step of every
 //   (sequence, head) at its position pos[b] on the caller's fp32 state, GroupNorm,
 //   the swish gate, then y = Z W_O^T; pos[b] += 1 on the device when advance_pos.
 ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, const void *w_v, const void *w_g,
@@ -257,13 +263,18 @@ ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, con
   hipStream_t st = (hipStream_t)hip_stream;
   char *ws = (char *)workspace;
   const long long NP = 2LL * H * dk + 2LL * H * dv;
-  uint16_t *proj = (uint16_t *)ws, *z = (uint16_t *)(ws + align256((size_t)B * NP * 2));
-  void *blas = ws + align256((size_t)B * NP * 2) + align256((size_t)B * H * dv * 2);
+  // the step's projections stay fp32: a (token, head) row whose retention output
+  // nearly cancels is divided by its small deviation in GroupNorm, which would
+  // magnify the bf16 rounding of q and k
+  float *proj = (float *)ws;
+  uint16_t *z = (uint16_t *)(ws + align256((size_t)B * NP * 4));
+  void *blas = ws + align256((size_t)B * NP * 4) + align256((size_t)B * H * dv * 2);
   const long long cq = 0, ck = (long long)H * dk, cv = 2LL * H * dk, cg = cv + (long long)H * dv;
 
   // 1. projections of this step's tokens into P[B][NP]
   {
-    hipError_t e = projections((const uint16_t *)x, w_q, w_k, w_v, w_g, proj, B, d_model, H, dk, dv, blas, st);
+    hipError_t e =
+        projections(true, (const uint16_t *)x, w_q, w_k, w_v, w_g, proj, B, d_model, H, dk, dv, blas, st);
     if (e != hipSuccess) return launch_fail(e);
   }
 
@@ -274,7 +285,7 @@ ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, con
   a.k = proj + ck;
   a.v = proj + cv;
   a.o = z;
-  a.gate = proj + cg;
+  a.gate = (const uint16_t *)(proj + cg);
   a.gate_swish = 1;
   a.q_sb = NP;
   a.q_sh = dk;
@@ -294,7 +305,7 @@ ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, con
   a.dk = dk;
   a.dv = dv;
   a.chunk = 1;
-  a.in_bf16 = 1;
+  a.in_bf16 = 0;
   a.out_bf16 = 1;
   a.use_theta = theta != nullptr;
   a.use_gn = 1;
@@ -306,7 +317,7 @@ ret_status_t msr_layer_step(const void *x, const void *w_q, const void *w_k, con
   if (e != hipSuccess) return launch_fail(e);
 
   // 3. output projection, 4. positions
-  e = plain_gemm(z, (const uint16_t *)w_o, (uint16_t *)y, B, d_model, H * dv, d_model, blas, st);
+  e = plain_gemm(z, (const uint16_t *)w_o, y, B, d_model, H * dv, d_model, blas, st);
   if (e != hipSuccess) return launch_fail(e);
   if (advance_pos) {
     e = launch_advance_pos(pos, B, st);

@@ -50,7 +50,8 @@ __device__ __forceinline__ float score_vs_key(const RetArgs &a, const float *qro
 }
 
 // GroupNorm over the dv columns spread as acc[c] <-> column threadIdx.x + c*VT, then
-// the gate (when given; bf16 at element offset goff + column), then store.
+// the gate (when given; at element offset goff + column, bf16 or fp32 as the
+// inputs), then store.
 __device__ __forceinline__ void gn_store(const RetArgs &a, float *acc, long long ooff, float *red,
                                          long long goff = 0) {
   const int t = threadIdx.x;
@@ -72,7 +73,10 @@ __device__ __forceinline__ void gn_store(const RetArgs &a, float *acc, long long
   if (a.gate)
 #pragma unroll
     for (int c = 0; c < MAXC; ++c)
-      if (t + c * VT < a.dv) acc[c] *= gate_value(bf2f(a.gate[goff + t + c * VT]), a.gate_swish);
+      if (t + c * VT < a.dv) {
+        const long long gi = goff + t + c * VT;
+        acc[c] *= gate_value(a.in_bf16 ? bf2f(a.gate[gi]) : ((const float *)a.gate)[gi], a.gate_swish);
+      }
 #pragma unroll
   for (int c = 0; c < MAXC; ++c)
     if (t + c * VT < a.dv) store_elem(a.o, ooff + t + c * VT, acc[c], a.out_bf16);

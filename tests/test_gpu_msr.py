@@ -135,6 +135,24 @@ def test_msr_step_matches_layer(B, T, dm, H, dk, dv):
         _tol.assert_bf16(got[b:b + 1], ref, slice_dims=0, what=f"msr step b={b}")
 
 
+def test_msr_step_many_sequences():
+    """70 sequences per step: the step's GEMMs take one full 64-row tile and a
+    ragged one of 6 rows; 3 steps from a zero state against the oracle layer."""
+    B, T, dm, H, dk, dv = 70, 3, 256, 2, 64, 128
+    x = randn((B, T, dm), 870, 1.0, torch.bfloat16)
+    w = _step_weights(dm, H, dk, dv, 870)
+    g, th = multiscale_gamma(H), rotation_theta(dk)
+    wd = [t.to(DEV) for t in w]
+    state = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=DEV)
+    pos = torch.zeros(B, dtype=torch.int32, device=DEV)
+    got = torch.stack([rn.msr_layer_step(x[:, t].contiguous().to(DEV), *wd, state, pos, H, dk, dv, g, th,
+                                         gn_eps=1e-5) for t in range(T)], 1)
+    torch.cuda.synchronize()
+    ref = oracle.msr_layer(x, *w, H, dk, dv, g, th, pos0=0, gn_eps=1e-5)
+    _tol.assert_bf16(got[:64], ref[:64], slice_dims=0, what="msr step, first 64-row tile")
+    _tol.assert_bf16(got[64:], ref[64:], slice_dims=0, what="msr step, ragged 6-row tile")
+
+
 def test_msr_step_graph_replay():
     """One step captured as a graph (positions advanced on the device) and replayed
     once per token, with host copies and synchronisations between replays: every
