@@ -249,7 +249,7 @@ def bench_parallel(steps, warmup):
     return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3, **_spread(),
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / BF16_PEAK_TFLOPS, "traffic": _read_traffic("parallel_2k"),
-                         "kernel": "qblock_kernel<256,512,parallel> (hi+lo scores for the first query block of each sequence, bf16 for the rest)",
+                         "kernel": "retention_parallel call: rotate_keys_kernel (keys rotated once) + qblock_kernel<256,512,parallel> (hi+lo scores for the first query block of each sequence; keys by LDS-DMA, bf16 scores for the rest)",
                          "algorithmic_tflop_per_call": flops / 1e12}}
 
 
@@ -304,7 +304,7 @@ def copy_calibration(reps=3):
 _PMC_GROUPS = {
     "chunkwise_32k": (("ret::",), ("seg_out_kernel",)),
     "decode_step": (("vec_step_kernel",), ("vec_step_kernel",)),
-    "parallel_2k": (("qblock_kernel",), ("qblock_kernel<256, 512, true, false>",)),
+    "parallel_2k": (("qblock_kernel", "rotate_keys_kernel"), ("qblock_kernel<256, 512, true, false, true>",)),
     "chunkwise_bwd": (("ret::",), ("seg_state_kernel<128, 256>",)),
     "msr_layer": (("ret::", "Cijk"), ("seg_scan_t_kernel",)),
     "msr_decode": (("ret::", "Cijk"), ("vec_step_kernel",)),

@@ -1,8 +1,8 @@
 """The bench's HBM-traffic summary (bench.pmc_summary) on synthetic rocprofv3
 counter files: per-call bytes are the sum over the kernels of one call divided
 by the number of calls, each counter scaled by its reading for the calibration
-copy.  The parallel form launches two query-block kernels per call (the hi+lo
-first blocks and the rest); only the second counts the calls."""
+copy.  The parallel form launches the key rotation and two query-block kernels
+per call (the hi+lo first blocks and the rest); only the last counts the calls."""
 import csv
 import os
 
@@ -34,20 +34,23 @@ def _summary(tmp_path, name, fetch_rows, write_rows):
 
 def test_parallel_calls_counted_once(tmp_path):
     copy_kib = bench.COPY_BYTES / 1024
-    main = "void ret::qblock_kernel<256, 512, true, false>(ret::RetArgs, ret::TaskGeom, unsigned short const*)"
-    first = "void ret::qblock_kernel<256, 512, true, true>(ret::RetArgs, ret::TaskGeom, unsigned short const*)"
+    main = ("void ret::qblock_kernel<256, 512, true, false, true>(ret::RetArgs, ret::TaskGeom, unsigned short const*, "
+            "unsigned short const*)")
+    first = ("void ret::qblock_kernel<256, 512, true, true, false>(ret::RetArgs, ret::TaskGeom, unsigned short const*, "
+             "unsigned short const*)")
+    rot = "void ret::rotate_keys_kernel<256>(ret::RetArgs, unsigned short*)"
     ncalls = 3
     # fetch: the counter reads half the bytes (factor 2), write reads them all
     fetch = [("void at::native::neg_kernel", copy_kib / 2)]
     write = [("void at::native::neg_kernel", copy_kib)]
     for _ in range(ncalls):
-        fetch += [(first, 100.0), (main, 900.0)]
-        write += [(first, 10.0), (main, 290.0)]
+        fetch += [(rot, 50.0), (first, 100.0), (main, 900.0)]
+        write += [(rot, 40.0), (first, 10.0), (main, 290.0)]
     vals = _summary(tmp_path, "parallel_2k", fetch, write)
-    assert float(vals["fetch_kib_per_call"]) == 1000.0
-    assert float(vals["write_kib_per_call"]) == 300.0
+    assert float(vals["fetch_kib_per_call"]) == 1050.0
+    assert float(vals["write_kib_per_call"]) == 340.0
     assert abs(float(vals["fetch_factor"]) - 2.0) < 1e-9 and abs(float(vals["write_factor"]) - 1.0) < 1e-9
-    assert int(vals["hbm_bytes_per_call"]) == (2 * 1000 + 300) * 1024
+    assert int(vals["hbm_bytes_per_call"]) == (2 * 1050 + 340) * 1024
 
 
 def test_chunkwise_three_kernels_per_call(tmp_path):
