@@ -88,6 +88,10 @@ const char *retention_last_error(void);
  *   o    : [B,H,L,dv] out_dtype (must not alias an input)
  * bf16 inputs with (dk, dv) in {(64,128),(128,128),(128,256),(256,256),
  * (256,512)} use the MFMA kernels; every other case uses the vector (FMA) kernels.
+ * With rotation on the MFMA path the keys are rotated once per call into
+ * B*H*L*dk bf16 of scratch taken stream-ordered from the device's default memory
+ * pool (hipMallocAsync / hipFreeAsync on hip_stream; the pool is told once to
+ * keep freed memory); RET_ERR_HIP if that allocation fails.
  * L == 0 is a no-op.
  */
 ret_status_t retention_parallel(const void *q, const void *k, const void *v, void *o, int B,
