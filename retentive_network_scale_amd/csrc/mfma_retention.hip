@@ -1430,11 +1430,153 @@ __global__ __launch_bounds__(NT) void seg_state_kernel(RetArgs a, TaskGeom geo, 
 }
 
 // ---------------------------------------------------------------- pass 2: scan over segments
-// Exclusive scan over a (b, h)'s segments of S <- gamma^len S + S_own(segment).
+// The state entering each segment of a (b, h) follows the linear recurrence
+//   S(s + 1) = g_s S(s) + A_s,   g_s = gamma^len(s),   S(0) = the incoming state,
+// with A_s the segment's own state from pass 1 ("Retentive Network" paper
+// summary, Sec. 2.1 (3): the state carried from chunk to chunk, taken over
+// whole segments).  Each step is an affine map x -> g x + A, and maps compose
+// associatively: (g1, A1) then (g2, A2) is (g2 g1, g2 A1 + A2).  So the scan runs
+// across the lanes of a wave: every state element (column) is held by NL
+// lanes, lane j composing the maps of its R consecutive segments R j ..
+// R j + R - 1 in registers; log2(NL) steps of cross-lane moves (DPP row
+// shifts, no LDS traffic) compose the lanes' maps (inclusive scan), and the map
+// of lanes 0 .. j-1 applied to the incoming state is the state entering lane
+// j's first segment, from which the lane walks its segments again.
+//
 // seg_scan_kernel (state kept in registers by the output kernel): in place,
 // ws[bh][s] holds the segment's own state on entry and the state entering
-// segment s on exit.  Both write the state after the last token.
+// segment s on exit, plus the state after the last segment in state_out.
+// Lane (j, cg) of a wave takes the U consecutive elements of column group cg
+// for segments R j .. R j + R - 1, loaded and stored as float4 runs straight
+// from and to memory (the NL lanes of a group read U * 4 * (64 / NL) contiguous
+// bytes of NL * R rows); all the scan's data stay in registers.  NSP: segments
+// rounded up to a power of two.
+
+// x from lane (lane - D) of the same 16-lane row (DPP row_shr:D); lanes
+// whose source lies outside the row keep their own value.
+template <int D>
+__device__ __forceinline__ float lane_shr(float x) {
+  static_assert(D >= 1 && D <= 15, "row shift");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                                               0x110 + D, 0xF, 0xF, false));
+}
+
+// Lanes per state element for NSP segments: few lanes keep the per-element
+// overhead of the cross-lane steps low (four lanes of eight segments at 32).
+__host__ __device__ constexpr int scan_lanes(int nsp) { return nsp <= 4 ? nsp : (nsp <= 32 ? 4 : (nsp <= 128 ? nsp / 8 : 16)); }
+
+template <int NSP>
 __global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, float *ws, const float *state_in,
+                                                       float *state_out) {
+  // lanes per column: a power of two within one 16-lane DPP row, R <= 16 segments each
+  constexpr int NL = scan_lanes(NSP);
+  constexpr int R = NSP / NL;
+  constexpr int U = R <= 8 ? 8 : 4;       // consecutive elements per lane
+  constexpr int CB = 4 * (64 / NL) * U;   // elements per block
+  static_assert(NL <= 16 && U % 4 == 0, "lane layout");
+  const long long E = (long long)a.dk * a.dv;
+  const int bh = blockIdx.y, nseg = geo.nseg;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = lane % NL, cg = lane / NL;
+  const long long e0 = (long long)blockIdx.x * CB + ((long long)w * (64 / NL) + cg) * U;  // the lane's first element
+  const bool live = e0 < E;  // E is a multiple of U
+  float *base = ws + (long long)bh * nseg * E + e0;
+  // the incoming state first, then the segments in order, all in flight together
+  float sv[U];
+#pragma unroll
+  for (int q = 0; q < U / 4; ++q) {
+    const float4 x = (live && state_in) ? *(const float4 *)(state_in + (long long)bh * E + e0 + 4 * q)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    sv[4 * q] = x.x;
+    sv[4 * q + 1] = x.y;
+    sv[4 * q + 2] = x.z;
+    sv[4 * q + 3] = x.w;
+  }
+  float A[R][U];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int sg = j * R + r;
+#pragma unroll
+    for (int q = 0; q < U / 4; ++q) {
+      const float4 x = (live && sg < nseg) ? *(const float4 *)(base + (long long)sg * E + 4 * q)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      A[r][4 * q] = x.x;
+      A[r][4 * q + 1] = x.y;
+      A[r][4 * q + 2] = x.z;
+      A[r][4 * q + 3] = x.w;
+    }
+  }
+  const float lg = safe_log2(a.gamma[bh % a.H]);
+  const int seg_len = geo.seg_chunks * a.chunk;
+  float gs[R];  // g of the lane's segments; padding segments are the identity map
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int sg = j * R + r;
+    gs[r] = sg < nseg ? dpow(lg, min(a.L, (sg + 1) * seg_len) - sg * seg_len) : 1.0f;
+  }
+  // the lane's segments composed, per element: state after = G * state before + X
+  float X[U], G = 1.0f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) X[u] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) X[u] = gs[r] * X[u] + A[r][u];
+    G *= gs[r];
+  }
+  // inclusive composition over lanes 0 .. j of the group (G is the same for
+  // every element of a lane)
+#define RET_SCAN_STEP(D)                                   \
+  if constexpr (NL > D) {                                  \
+    const float Gp = lane_shr<D>(G);                       \
+    float Xp[U];                                           \
+    _Pragma("unroll") for (int u = 0; u < U; ++u) Xp[u] = lane_shr<D>(X[u]); \
+    if (j >= D) {                                          \
+      _Pragma("unroll") for (int u = 0; u < U; ++u) X[u] = G * Xp[u] + X[u]; \
+      G *= Gp;                                             \
+    }                                                      \
+  }
+  RET_SCAN_STEP(1)
+  RET_SCAN_STEP(2)
+  RET_SCAN_STEP(4)
+  RET_SCAN_STEP(8)
+#undef RET_SCAN_STEP
+  // the state entering segment R j: lanes 0 .. j-1 applied to the incoming state
+  float run[U];
+  {
+    const float Ge = lane_shr<1>(G);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float Xe = lane_shr<1>(X[u]);
+      run[u] = (NL > 1 && j > 0) ? Ge * sv[u] + Xe : sv[u];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int sg = j * R + r;
+#pragma unroll
+    for (int q = 0; q < U / 4; ++q)
+      if (live && sg < nseg)
+        *(float4 *)(base + (long long)sg * E + 4 * q) =
+            make_float4(run[4 * q], run[4 * q + 1], run[4 * q + 2], run[4 * q + 3]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) run[u] = gs[r] * run[u] + A[r][u];
+  }
+  if (j == NL - 1 && live && state_out)
+#pragma unroll
+    for (int q = 0; q < U / 4; ++q)
+      *(float4 *)(state_out + (long long)bh * E + e0 + 4 * q) =
+          make_float4(run[4 * q], run[4 * q + 1], run[4 * q + 2], run[4 * q + 3]);
+}
+
+// seg_scan_seq_kernel: the same scan with one thread per four state elements
+// walking all segments in order (loads of SB segments in flight, each prefix
+// stored as soon as it is known).  It does the least arithmetic and streams
+// best, so it is taken whenever the (b, h) x element columns alone give a
+// thread to every lane of the GPU (about one 256-thread block per CU); with
+// fewer heads the wavefront-level scan above spreads each column's segments
+// over several lanes instead.
+__global__ __launch_bounds__(256) void seg_scan_seq_kernel(RetArgs a, TaskGeom geo, float *ws, const float *state_in,
                                                        float *state_out) {
   const long long SZ = (long long)a.dk * a.dv;
   const long long n4 = SZ / 4;
@@ -1466,6 +1608,40 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(RetArgs a, TaskGeom geo, 
     }
     if (state_out) ((float4 *)(state_out + (long long)bh * SZ))[e] = run;
   }
+}
+
+
+template <int NSP>
+static void launch_seg_scan(const RetArgs &a, const TaskGeom &geo, float *ws, const float *state_in, float *state_out,
+                            hipStream_t st) {
+  constexpr int NL = scan_lanes(NSP), R = NSP / NL, U = R <= 8 ? 8 : 4;
+  constexpr int CB = 4 * (64 / NL) * U;
+  const long long E = (long long)a.dk * a.dv;
+  hipLaunchKernelGGL(seg_scan_kernel<NSP>, dim3((unsigned)((E + CB - 1) / CB), a.B * a.H), dim3(256), 0, st, a, geo,
+                     ws, state_in, state_out);
+}
+
+// Segments per (b, h) are at most 256 (the segment target below).
+static hipError_t run_seg_scan(const RetArgs &a, const TaskGeom &geo, float *ws, const float *state_in,
+                               float *state_out, hipStream_t st) {
+  const int n = geo.nseg;
+  const long long n4 = (long long)a.dk * a.dv / 4, seq_blocks = (n4 + 255) / 256 * a.B * a.H;
+  if (seq_blocks >= 256 || n <= 1) {  // a block of the sequential scan for every CU
+    hipLaunchKernelGGL(seg_scan_seq_kernel, dim3((unsigned)((n4 + 255) / 256), a.B * a.H), dim3(256), 0, st, a, geo,
+                       ws, state_in, state_out);
+    return hipGetLastError();
+  }
+  if (n <= 1) launch_seg_scan<1>(a, geo, ws, state_in, state_out, st);
+  else if (n <= 2) launch_seg_scan<2>(a, geo, ws, state_in, state_out, st);
+  else if (n <= 4) launch_seg_scan<4>(a, geo, ws, state_in, state_out, st);
+  else if (n <= 8) launch_seg_scan<8>(a, geo, ws, state_in, state_out, st);
+  else if (n <= 16) launch_seg_scan<16>(a, geo, ws, state_in, state_out, st);
+  else if (n <= 32) launch_seg_scan<32>(a, geo, ws, state_in, state_out, st);
+  else if (n <= 64) launch_seg_scan<64>(a, geo, ws, state_in, state_out, st);
+  else if (n <= 128) launch_seg_scan<128>(a, geo, ws, state_in, state_out, st);
+  else if (n <= 256) launch_seg_scan<256>(a, geo, ws, state_in, state_out, st);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // seg_scan_t_kernel (states handed to the query-block kernel): the state
@@ -1757,9 +1933,8 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (in_regs) {
-    const long long n4 = (long long)a.dk * a.dv / 4;
-    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)((n4 + 255) / 256), a.B * a.H), dim3(256), 0, st, a, geo, seg,
-                       state_in, state_out);
+    e = run_seg_scan(a, geo, seg, state_in, state_out, st);
+    if (e != hipSuccess) return e;
   } else {
     static_assert(DK % 64 == 0 && DV % 64 == 0, "64 x 64 scan tiles");
     hipLaunchKernelGGL(seg_scan_t_kernel, dim3((DK / 64) * (DV / 64), a.B * a.H), dim3(256), 0, st, a, geo, seg, sinT,
