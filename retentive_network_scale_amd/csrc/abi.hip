@@ -425,16 +425,32 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
   if (use_mfma(dk, dv, in_dtype) && use_mfma(dv, dk, in_dtype) && chunk_state_in_regs(B, H, L, dk, dv, chunk) &&
       chunk_state_in_regs(B, H, L, dv, dk, chunk)) {
     // the MFMA kernels read the reversed sequences themselves: only the rotated
-    // keys and queries are prepared (forward order; the p.kr and p.qrev slots)
-    void *kr = ws + p.kr, *qr = ws + p.qrev;
-    if ((e = launch_bwd_prep(k, kr, nullptr, rows, L, dk, rot, pos0, bf, th, st)) != hipSuccess ||
-        (e = launch_bwd_prep(q, qr, nullptr, rows, L, dk, rot, pos0, bf, th, st)) != hipSuccess ||
-        (e = bwd_retention(d_o, v, kr, dq, dqr, B, H, L, dv, dk, chunk, gamma, theta, pos0, true, false, in_dtype,
-                           out_dtype, cws, st)) != hipSuccess ||
-        (e = bwd_retention(v, d_o, qr, dk_out, dkr, B, H, L, dv, dk, chunk, gamma, theta, pos0, true, true, in_dtype,
-                           out_dtype, cws, st, true)) != hipSuccess ||
+    // keys and queries are prepared (forward order; the p.kr and p.qrev slots).
+    // The dv sum's state, sum over later tokens of q~^T dO, is the transpose of
+    // the dk~ sum's, sum of dO^T q~ (same segments, same decay): the dv sum runs
+    // first, and the dk~ sum's output pass reads the states it left in the
+    // workspace, transposed, instead of a state pass and a scan of its own.
+    // Without rotation the sums read k and q themselves.
+    const void *kr = rot ? (const void *)(ws + p.kr) : k, *qr = rot ? (const void *)(ws + p.qrev) : q;
+    e = rot ? launch_bwd_prep2(k, ws + p.kr, q, ws + p.qrev, rows, L, dk, pos0, bf, th, st) : hipSuccess;
+    if (e != hipSuccess ||
         (e = bwd_retention(kr, qr, d_o, dv_out, dvr, B, H, L, dk, dv, chunk, gamma, nullptr, pos0, false, true,
                            in_dtype, out_dtype, cws, st, true)) != hipSuccess)
+      return hip_status(e);
+    {
+      RetArgs a = make_args(v, d_o, qr, dk_out, B, H, L, dv, dk, chunk, gamma, nullptr, pos0, -1.0f, in_dtype,
+                            out_dtype);
+      a.in_rev = 1;
+      a.out_rev = 1;
+      a.out_rot = rot;
+      if (rot)
+        for (int i = 0; i < dk / 2; ++i) a.theta[i] = theta[i];
+      a.state_t = 1;
+      if ((e = launch_mfma_chunkwise_out(a, chunk_plan(B, H, L, dv, dk, chunk), cws, st)) != hipSuccess)
+        return hip_status(e);
+    }
+    if ((e = bwd_retention(d_o, v, kr, dq, dqr, B, H, L, dv, dk, chunk, gamma, theta, pos0, true, false, in_dtype,
+                           out_dtype, cws, st)) != hipSuccess)
       return hip_status(e);
     return ok();
   }

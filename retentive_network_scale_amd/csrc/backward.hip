@@ -68,6 +68,66 @@ __global__ void bwd_prep_kernel(const E *x, E *dst_fwd, E *dst_rev, long long ro
   }
 }
 
+// Two tensors of the same shape rotated at the same positions in one pass
+// (the backward's K~ and Q~ in forward order): one thread per 8 consecutive
+// elements of both, one angle reduction and one sine/cosine per pair serving
+// both.  dst_a[r] = R_n a[r], dst_b[r] = R_n b[r].
+template <typename E>
+__device__ __forceinline__ void load8(const E *p, float (&v)[8]) {
+  if constexpr (sizeof(E) == 2) {
+    const uint4 raw = *(const uint4 *)p;
+    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(wv[e] << 16);
+      v[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+    }
+  } else {
+    const float4 lo = *(const float4 *)p, hi = *(const float4 *)(p + 4);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ void store8(E *p, const float (&v)[8]) {
+  if constexpr (sizeof(E) == 2) {
+    *(uint4 *)p = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+  } else {
+    *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4 *)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+template <typename E>
+__global__ void bwd_prep2_kernel(const E *xa, E *dst_a, const E *xb, E *dst_b, long long rows, int L, int d,
+                                 long long pos0, RetArgs th) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int c8s = d / 8;
+  if (i >= rows * c8s) return;
+  const long long row = i / c8s;
+  const int c8 = (int)(i % c8s);
+  const int n = (int)(row % L);
+  const long long off = row * d + 8 * c8;
+  float va[8], vb[8];
+  load8(xa + off, va);
+  load8(xb + off, vb);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float c, sn;
+    rot_cs<false>(pos0 + n, th.theta[4 * c8 + j], c, sn);
+    float re = va[2 * j], im = va[2 * j + 1];
+    va[2 * j] = re * c - im * sn;
+    va[2 * j + 1] = re * sn + im * c;
+    re = vb[2 * j];
+    im = vb[2 * j + 1];
+    vb[2 * j] = re * c - im * sn;
+    vb[2 * j + 1] = re * sn + im * c;
+  }
+  store8(dst_a + off, va);
+  store8(dst_b + off, vb);
+}
+
 // out[n] = R_n^T src[rev ? L-1-n : n] (R = identity unless rot); src fp32.
 __global__ void bwd_final_kernel(const float *src, void *out, long long rows, int L, int d, int rev, int rot,
                                  long long pos0, int out_bf16, RetArgs th) {
@@ -100,6 +160,19 @@ hipError_t launch_bwd_prep(const void *x, void *dst_fwd, void *dst_rev, long lon
   else
     hipLaunchKernelGGL(bwd_prep_kernel<float>, grid, dim3(256), 0, st, (const float *)x, (float *)dst_fwd,
                        (float *)dst_rev, rows, L, d, (int)rot, pos0, th);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep2(const void *xa, void *dst_a, const void *xb, void *dst_b, long long rows, int L, int d,
+                            long long pos0, bool bf16, const RetArgs &th, hipStream_t st) {
+  const long long n = rows * (d / 8);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(bwd_prep2_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)xa, (uint16_t *)dst_a,
+                       (const uint16_t *)xb, (uint16_t *)dst_b, rows, L, d, pos0, th);
+  else
+    hipLaunchKernelGGL(bwd_prep2_kernel<float>, grid, dim3(256), 0, st, (const float *)xa, (float *)dst_a,
+                       (const float *)xb, (float *)dst_b, rows, L, d, pos0, th);
   return hipGetLastError();
 }
 

@@ -28,6 +28,9 @@ struct RetArgs {
   // Input reversal (segment-state and segment-output kernels, no rotation): the
   // kernels' token n is row L-1-n of q, k and v
   int in_rev;
+  // Segment-output pass run on its own (launch_mfma_chunkwise_out): the states
+  // entering the segments were written as [dv][dk] by a call with dk and dv swapped
+  int state_t;
   long long q_sb, q_sh, q_sn;
   long long v_sb, v_sh, v_sn;
   long long o_sb, o_sh, o_sn;

@@ -17,6 +17,9 @@ hipError_t launch_vec_step(const RetArgs &a, float *state, const int *pos, hipSt
 // [rows, L, d] tensor; un-rotate (and reverse) an fp32 gradient into out.
 hipError_t launch_bwd_prep(const void *x, void *dst_fwd, void *dst_rev, long long rows, int L, int d, bool rot,
                            long long pos0, bool bf16, const RetArgs &th, hipStream_t st);
+// dst_a = R x_a and dst_b = R x_b (forward order, rotation on) in one pass.
+hipError_t launch_bwd_prep2(const void *xa, void *dst_a, const void *xb, void *dst_b, long long rows, int L, int d,
+                            long long pos0, bool bf16, const RetArgs &th, hipStream_t st);
 hipError_t launch_bwd_final(const float *src, void *out, long long rows, int L, int d, bool rev, bool rot,
                             long long pos0, bool out_bf16, const RetArgs &th, hipStream_t st);
 // pos[b] += 1 for b < B (device positions of decode steps)
@@ -43,6 +46,11 @@ bool chunk_state_in_regs(int B, int H, int L, int dk, int dv, int chunk);
 // own (created on first use); false keeps every launch on st.
 hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &plan, void *ws,
                                  const float *state_in, float *state_out, hipStream_t st, bool fork = true);
+// Design A's segment-output pass alone (plan.in_regs), on the states entering
+// each segment already in ws; with a.state_t they are read transposed, as left
+// by launch_mfma_chunkwise on the same sequence with dk and dv swapped (the
+// backward's dk and dv sums carry transposed states).
+hipError_t launch_mfma_chunkwise_out(const RetArgs &a, const ChunkPlan &plan, void *ws, hipStream_t st);
 
 // Plain bf16 GEMM through hipBLASLt (blaslt.hip): C[t][n] = sum_k X[t][k] W[n][k]
 // (+ R[t][n] when R is given, same layout as C) for t < T, n < N, row-major with

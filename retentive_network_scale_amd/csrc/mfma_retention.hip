@@ -1109,13 +1109,23 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
   const int t_hi = min(a.L, (c_lo + geo.seg_chunks) * a.chunk);
   {
     const float *S_in = seg_state + ((long long)bh * geo.nseg + seg) * DK * DV;
+    if (a.state_t) {  // stored [DV][DK]: a lane's four rows are 16 contiguous bytes
 #pragma unroll
-    for (int dkb = 0; dkb < DKB; ++dkb)
+      for (int dkb = 0; dkb < DKB; ++dkb)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb) {
+          const float4 x = *(const float4 *)(S_in + (long long)(w * RW + dv_of<PAIR>(rb, l16)) * DK + 16 * dkb + 4 * g);
+          st[dkb][rb] = f32x4{x.x, x.y, x.z, x.w};
+        }
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          st[dkb][rb][i] = S_in[(long long)(16 * dkb + 4 * g + i) * DV + w * RW + dv_of<PAIR>(rb, l16)];
+      for (int dkb = 0; dkb < DKB; ++dkb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            st[dkb][rb][i] = S_in[(long long)(16 * dkb + 4 * g + i) * DV + w * RW + dv_of<PAIR>(rb, l16)];
+    }
   }
   TileIO<DK> qio, kio;
   RowIO<DV> vio;
@@ -1918,6 +1928,21 @@ static hipError_t run_qblocks(const RetArgs &a, TaskGeom geo, bool par, const ui
   return e;
 }
 
+// The segment-output pass of design A: hi+lo scores when GroupNorm follows
+// rotation (or a head decays fast), resident keys when they fit, else plain.
+template <int DK, int DV>
+static hipError_t launch_seg_out(const RetArgs &a, TaskGeom geo, const float *seg, hipStream_t st) {
+  geo.ntasks = a.B * a.H * geo.nseg;
+  const dim3 grid(xcd_grid(geo.ntasks));
+  if ((a.use_gn && a.use_theta) || split_all_blocks(a))
+    hipLaunchKernelGGL((seg_out_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, seg);
+  else if (DK <= 128 && a.chunk <= KRES * BT)  // resident keys fit in LDS for DK <= 128
+    hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, (DK <= 128)>), grid, dim3(NT), 0, st, a, geo, seg);
+  else
+    hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, seg);
+  return hipGetLastError();
+}
+
 template <int DK, int DV>
 static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, const float *state_in,
                                 float *state_out, hipStream_t st, bool fork) {
@@ -1944,17 +1969,22 @@ static hipError_t run_chunkwise(const RetArgs &a, const ChunkPlan &p, char *ws, 
   if (e != hipSuccess) return e;
   if constexpr (FITS) {
     if (!in_regs) return run_qblocks<DK, DV>(a, geo, false, sinT, st, fork);
-    geo.ntasks = a.B * a.H * geo.nseg;
-    const dim3 grid(xcd_grid(geo.ntasks));
-    if ((a.use_gn && a.use_theta) || split_all_blocks(a))
-      hipLaunchKernelGGL((seg_out_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, seg);
-    else if (DK <= 128 && a.chunk <= KRES * BT)  // resident keys fit in LDS for DK <= 128
-      hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, (DK <= 128)>), grid, dim3(NT), 0, st, a, geo, seg);
-    else
-      hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, seg);
-    return hipGetLastError();
+    return launch_seg_out<DK, DV>(a, geo, seg, st);
   } else {
     return run_qblocks<DK, DV>(a, geo, false, sinT, st, fork);
+  }
+}
+
+// Design A's output pass alone, on the states entering each segment already in
+// ws (RetArgs::state_t: written transposed by a call with dk and dv swapped).
+template <int DK, int DV>
+static hipError_t run_chunkwise_out(const RetArgs &a, const ChunkPlan &p, char *ws, hipStream_t st) {
+  if constexpr ((long long)DK * DV <= IN_REGS_MAX) {
+    if (!p.in_regs) return hipErrorNotSupported;
+    TaskGeom geo{p.nseg, p.seg_chunks, 1, 1, 0, (a.L + a.chunk - 1) / a.chunk};
+    return launch_seg_out<DK, DV>(a, geo, (float *)ws, st);
+  } else {
+    return hipErrorNotSupported;
   }
 }
 
@@ -1966,6 +1996,15 @@ hipError_t launch_mfma_parallel(const RetArgs &a, hipStream_t st) {
   if (a.dk == 256 && a.dv == 128) return run_qblocks<256, 128>(a, geo, true, nullptr, st, false);
   if (a.dk == 256 && a.dv == 256) return run_qblocks<256, 256>(a, geo, true, nullptr, st, false);
   if (a.dk == 256 && a.dv == 512) return run_qblocks<256, 512>(a, geo, true, nullptr, st, false);
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_mfma_chunkwise_out(const RetArgs &a, const ChunkPlan &p, void *ws, hipStream_t st) {
+  char *w = (char *)ws;
+  if (a.dk == 64 && a.dv == 128) return run_chunkwise_out<64, 128>(a, p, w, st);
+  if (a.dk == 128 && a.dv == 128) return run_chunkwise_out<128, 128>(a, p, w, st);
+  if (a.dk == 128 && a.dv == 256) return run_chunkwise_out<128, 256>(a, p, w, st);
+  if (a.dk == 256 && a.dv == 128) return run_chunkwise_out<256, 128>(a, p, w, st);
   return hipErrorNotSupported;
 }
 
