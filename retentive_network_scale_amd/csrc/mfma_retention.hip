@@ -594,6 +594,17 @@ __device__ __forceinline__ void store_staged(const RetArgs &a, const uint16_t *O
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void *)((uint16_t *)a.o + obase + nbase * a.o_sn), (short)0, range,
                                         0x00020000);
+  // the gate's pieces first, all in flight together (rows past nvalid read the
+  // last valid row; their results are dropped)
+  u32x4 gt[NPT];
+  if (a.gate) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int c = tid + NT * i, row = min(c / C8, max(nvalid - 1, 0)), col = 8 * (c % C8);
+      gt[i] = *(const u32x4 *)(a.gate + (long long)b * a.g_sb + (long long)h * a.g_sh + (long long)(q0 + row) * a.g_sn +
+                               col);
+    }
+  }
   u32x4 o[NPT];
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
@@ -604,7 +615,6 @@ __device__ __forceinline__ void store_staged(const RetArgs &a, const uint16_t *O
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int c = tid + NT * i, row = c / C8, col = 8 * (c % C8);
-      if (row >= nvalid) continue;
       const uint32_t ow[4] = {o[i].x, o[i].y, o[i].z, o[i].w};
       float x[8];
 #pragma unroll
@@ -613,8 +623,7 @@ __device__ __forceinline__ void store_staged(const RetArgs &a, const uint16_t *O
         x[2 * e + 1] = __uint_as_float(ow[e] & 0xffff0000u);
       }
       if (a.gate) {
-        const long long go = (long long)b * a.g_sb + (long long)h * a.g_sh + (long long)(q0 + row) * a.g_sn + col;
-        const u32x4 gg = *(const u32x4 *)(a.gate + go);
+        const u32x4 gg = gt[i];
         const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -899,6 +908,19 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   TileIO<DK> qio, kio;
   if constexpr (QV) k_dma<DK>(Ks, ksrc + (long long)c0 * ksn, ksn, min(BT, Cc));
   qio.fetch(q + (long long)q0 * a.q_sn, a.q_sn, min(BT, c0 + Cc - q0));
+  // The cross term's A operands (rows S_c^T[w*RW + 16rb + l16][dk] of the state
+  // entering the chunk; inside each 32-wide k-step lane group g takes k = 8g ..
+  // 8g+7 for both operands, so every load is 16 contiguous bytes): all of them
+  // are issued here, behind the query tile, so their latency overlaps the
+  // prologue instead of stalling every k-step of the cross term.
+  u32x4 sa[PAR ? 1 : KS][RB];
+  if constexpr (!PAR) {
+    const uint16_t *s_t = SinT + ((long long)bh * geo.nchunks + c) * DK * DV + (long long)(w * RW + l16) * DK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sa[ks][rb] = *(const u32x4 *)(s_t + 16 * rb * DK + 32 * ks);
+  }
   if constexpr (!KPRE) kio.fetch(k + (long long)c0 * a.q_sn, a.q_sn, min(BT, Cc));
   __syncthreads();
   qio.template commit<true, false, SPLIT>(rot, a.pos0 + q0, theta_s, step_s, Qs, LDQ, KsL, nullptr, false, 0.f, 0);
@@ -917,26 +939,16 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
 #pragma unroll
     for (int qb4 = 0; qb4 < 4; ++qb4) ot[rb][qb4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (!PAR) {
-    // cross term gamma^(j+1) q S_c.  A operand rows: S_c^T[w*RW + 16rb + l16][dk];
-    // inside each 32-wide k-step lane group g takes k = 8g..8g+7 (for both
-    // operands), so every A load is 16 contiguous bytes straight from memory.
-    // The loads of step ks+1 are issued before the MFMAs of step ks.
-    const uint16_t *s_t = SinT + ((long long)bh * geo.nchunks + c) * DK * DV + (long long)(w * RW + l16) * DK + 8 * g;
-    u32x4 sa[2][RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sa[0][rb] = *(const u32x4 *)(s_t + 16 * rb * DK);
+    // cross term gamma^(j+1) q S_c, A operands prefetched above
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sa[(ks + 1) & 1][rb] = *(const u32x4 *)(s_t + 16 * rb * DK + 32 * (ks + 1));
 #pragma unroll
       for (int qb4 = 0; qb4 < 4; ++qb4) {
         const uint16_t *qr = Qs + (16 * qb4 + l16) * LDQ + 32 * ks + 8 * g;
         const u32x2 lo = *(const u32x2 *)qr, hi = *(const u32x2 *)(qr + 4);
         const u32x4 bq = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = mfma(sa[ks & 1][rb], bq, ot[rb][qb4]);
+        for (int rb = 0; rb < RB; ++rb) ot[rb][qb4] = mfma(sa[ks][rb], bq, ot[rb][qb4]);
       }
     }
 #pragma unroll
