@@ -308,6 +308,7 @@ _PMC_GROUPS = {
     "chunkwise_bwd": (("ret::",), ("seg_state_kernel<128, 256>",)),
     "msr_layer": (("ret::", "Cijk"), ("seg_scan_t_kernel",)),
     "msr_decode": (("ret::", "Cijk"), ("vec_step_kernel",)),
+    "retnet_block": (("ret::", "Cijk"), ("gelu_bf16_kernel",)),
 }
 
 
@@ -322,6 +323,14 @@ def _alg_bytes_msr():
     from workloads import MSR_LAYER as wl
     T = wl.B * wl.L
     return 2 * (2 * T * wl.d_model + wl.d_model * (2 * wl.H * wl.dk + 3 * wl.H * wl.dv))
+
+
+def _alg_bytes_block():
+    """The residual block's minimum: X and the seven weights read once, the block's
+    output written once (FFN width 2 d_model, as bench_block runs it)."""
+    from workloads import MSR_LAYER as wl
+    T, dff = wl.B * wl.L, 2 * wl.d_model
+    return 2 * (2 * T * wl.d_model + wl.d_model * (2 * wl.H * wl.dk + 3 * wl.H * wl.dv) + 2 * wl.d_model * dff)
 
 
 def _alg_bytes_msr_decode():
@@ -360,7 +369,7 @@ def pmc_summary(name, fetch_csv, write_csv, command, out_dir=None):
     hbm = f_kib * 1024 * f_fac + w_kib * 1024 * w_fac
     alg = {"chunkwise_32k": _alg_bytes_chunkwise, "decode_step": _alg_bytes_decode,
            "parallel_2k": _alg_bytes_parallel, "chunkwise_bwd": _alg_bytes_bwd, "msr_layer": _alg_bytes_msr,
-           "msr_decode": _alg_bytes_msr_decode}[name]()
+           "msr_decode": _alg_bytes_msr_decode, "retnet_block": _alg_bytes_block}[name]()
     out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{name}.txt")
     with open(out, "w") as fh:
         fh.write(f"# HBM traffic per call of {name}: rocprofv3 PMC FETCH_SIZE and WRITE_SIZE (KiB per dispatch),\n"
@@ -482,7 +491,7 @@ def bench_block(steps, warmup):
     tf = (gemm + ret + ffn) / per_call / 1e12
     return {"tokens_per_s": T / per_call, "ms_per_step": per_call * 1e3, "d_ffn": dff, **_spread(),
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": _read_traffic("retnet_block"),
                          "kernel": "retnet_block_fwd (LayerNorm, gated layer, residual GEMM, LayerNorm, FFN GEMMs "
                                    "with gelu, residual GEMM)",
                          "algorithmic_tflop_per_call": (gemm + ret + ffn) / 1e12}}
