@@ -213,6 +213,27 @@ def test_msr_step_full_layer_dims():
     _tol.assert_bf16(got, ref, slice_dims=0, what="msr step, layer dims")
 
 
+def test_msr_step_decode_batch_fused():
+    """The decode benchmark's step: 64 sequences at the layer workload's
+    dimensions with the four projection weights back to back (one fused GEMM of
+    12288 columns over d_model 2048, then the output GEMM over H dv = 4096), 2
+    steps from a zero state against the oracle layer, every sequence."""
+    wl = MSRWorkload()
+    B, T = 64, 2
+    _, wq, wk, wv, wg, wo = wl.inputs()
+    x = randn((B, T, wl.d_model), 5100, 1.0, torch.bfloat16)
+    g, th = wl.gamma(), wl.theta()
+    cat = torch.cat([wq, wk, wv, wg], 0).to(DEV)
+    fq, fk, fv, fg = torch.split(cat, [wl.H * wl.dk, wl.H * wl.dk, wl.H * wl.dv, wl.H * wl.dv], 0)
+    state = torch.zeros((B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=DEV)
+    pos = torch.zeros(B, dtype=torch.int32, device=DEV)
+    got = torch.stack([rn.msr_layer_step(x[:, t].contiguous().to(DEV), fq, fk, fv, fg, wo.to(DEV), state, pos, wl.H,
+                                         wl.dk, wl.dv, g, th, gn_eps=wl.gn_eps) for t in range(T)], 1)
+    torch.cuda.synchronize()
+    ref = oracle.msr_layer(x, wq, wk, wv, wg, wo, wl.H, wl.dk, wl.dv, g, th, pos0=0, gn_eps=wl.gn_eps)
+    _tol.assert_bf16(got, ref, slice_dims=0, what="msr decode batch, fused weights")
+
+
 def test_msr_fused_weights_match_separate():
     """Weights stored back to back (one fused projection matrix) take the
     single-GEMM path; layer and step outputs match the separate-weight path and
