@@ -140,6 +140,14 @@ size_t chunk_ws_bytes(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_
 // Backward workspace: rotated / reversed copies of the inputs (input dtype), the
 // three fp32 retention outputs and one chunkwise workspace shared by the three
 // retention calls (they run one after the other on the stream).
+// Chunk of the backward's inner retentions whose queries and keys are dv wide:
+// the longest chunk dividing the caller's whose keys stay resident in LDS
+// (segment boundaries, multiples of the caller's chunk, are kept).
+int bwd_wide_chunk(int dv, int chunk) {
+  const int r = resident_chunk_max(dv);
+  return chunk > r && chunk % r == 0 ? r : chunk;
+}
+
 struct BwdPlan {
   size_t kr, krev, qrev, vrev, dorev, dq, dk, dv, cws, cws_bytes, total;
 };
@@ -167,6 +175,7 @@ BwdPlan bwd_plan(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_t in_
   off += al(R * dv * 4);
   p.cws = off;
   p.cws_bytes = std::max(chunk_ws_bytes(B, H, L, dv, dk, chunk, in_dtype), chunk_ws_bytes(B, H, L, dk, dv, chunk, in_dtype));
+  p.cws_bytes = std::max(p.cws_bytes, chunk_ws_bytes(B, H, L, dv, dk, bwd_wide_chunk(dv, chunk), in_dtype));
   off += al(p.cws_bytes);
   p.total = off;
   return p;
@@ -437,8 +446,12 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
         (e = bwd_retention(kr, qr, d_o, dv_out, dvr, B, H, L, dk, dv, chunk, gamma, nullptr, pos0, false, true,
                            in_dtype, out_dtype, cws, st, true)) != hipSuccess)
       return hip_status(e);
+    const int cw = bwd_wide_chunk(dv, chunk);
     {
-      RetArgs a = make_args(v, d_o, qr, dk_out, B, H, L, dv, dk, chunk, gamma, nullptr, pos0, -1.0f, in_dtype,
+      // same segments as the dv sum's states, walked in chunks of cw
+      ChunkPlan pl = chunk_plan(B, H, L, dv, dk, chunk);
+      pl.seg_chunks *= chunk / cw;
+      RetArgs a = make_args(v, d_o, qr, dk_out, B, H, L, dv, dk, cw, gamma, nullptr, pos0, -1.0f, in_dtype,
                             out_dtype);
       a.in_rev = 1;
       a.out_rev = 1;
@@ -446,10 +459,9 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
       if (rot)
         for (int i = 0; i < dk / 2; ++i) a.theta[i] = theta[i];
       a.state_t = 1;
-      if ((e = launch_mfma_chunkwise_out(a, chunk_plan(B, H, L, dv, dk, chunk), cws, st)) != hipSuccess)
-        return hip_status(e);
+      if ((e = launch_mfma_chunkwise_out(a, pl, cws, st)) != hipSuccess) return hip_status(e);
     }
-    if ((e = bwd_retention(d_o, v, kr, dq, dqr, B, H, L, dv, dk, chunk, gamma, theta, pos0, true, false, in_dtype,
+    if ((e = bwd_retention(d_o, v, kr, dq, dqr, B, H, L, dv, dk, cw, gamma, theta, pos0, true, false, in_dtype,
                            out_dtype, cws, st)) != hipSuccess)
       return hip_status(e);
     return ok();

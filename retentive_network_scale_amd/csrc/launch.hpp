@@ -51,6 +51,9 @@ hipError_t launch_mfma_chunkwise(const RetArgs &a, const ChunkPlan &plan, void *
 // by launch_mfma_chunkwise on the same sequence with dk and dv swapped (the
 // backward's dk and dv sums carry transposed states).
 hipError_t launch_mfma_chunkwise_out(const RetArgs &a, const ChunkPlan &plan, void *ws, hipStream_t st);
+// Longest chunk whose keys design A's segment-output pass keeps resident in LDS
+// for query/key width dk.
+int resident_chunk_max(int dk);
 
 // Plain bf16 GEMM through hipBLASLt (blaslt.hip): C[t][n] = sum_k X[t][k] W[n][k]
 // (+ R[t][n] when R is given, same layout as C) for t < T, n < N, row-major with

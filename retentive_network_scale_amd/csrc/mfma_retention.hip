@@ -1075,6 +1075,9 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
 // diagonal visit; the update's zeta-scaled transposed copy of an earlier block
 // is rebuilt from LDS.
 constexpr int KRES = 4;  // resident key blocks: chunks up to 256 tokens
+// Resident key blocks that fit beside the other tiles in LDS: four for DK <= 128,
+// two (chunks up to 128 tokens) for DK = 256.
+constexpr int kres_of(int DK) { return DK <= 128 ? KRES : 2; }
 template <int DK, int DV, bool SPLIT, bool RES>
 __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, const float *seg_state) {
   using T = Tile<DK, DV>;
@@ -1088,7 +1091,7 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(RetArgs a, TaskGeom geo, co
   // (zeta-scaled keys of the update) only inside it: shared storage.
   constexpr int QK_SZ = BT * LDQ > BT * LDZ ? BT * LDQ : BT * LDZ;
   __shared__ __attribute__((aligned(16))) uint16_t QKs[QK_SZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[(RES ? KRES : 1) * BT * LDQ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[(RES ? kres_of(DK) : 1) * BT * LDQ];
   __shared__ __attribute__((aligned(16))) uint16_t KsL[SPLIT ? BT * LDQ : 8];
   __shared__ __attribute__((aligned(16))) uint16_t Vr[BT * LDV];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[BT * LDT];
@@ -1948,8 +1951,8 @@ static hipError_t launch_seg_out(const RetArgs &a, TaskGeom geo, const float *se
   const dim3 grid(xcd_grid(geo.ntasks));
   if ((a.use_gn && a.use_theta) || split_all_blocks(a))
     hipLaunchKernelGGL((seg_out_kernel<DK, DV, true, false>), grid, dim3(NT), 0, st, a, geo, seg);
-  else if (DK <= 128 && a.chunk <= KRES * BT)  // resident keys fit in LDS for DK <= 128
-    hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, (DK <= 128)>), grid, dim3(NT), 0, st, a, geo, seg);
+  else if (a.chunk <= kres_of(DK) * BT)  // the chunk's keys fit in LDS
+    hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, true>), grid, dim3(NT), 0, st, a, geo, seg);
   else
     hipLaunchKernelGGL((seg_out_kernel<DK, DV, false, false>), grid, dim3(NT), 0, st, a, geo, seg);
   return hipGetLastError();
@@ -2010,6 +2013,8 @@ hipError_t launch_mfma_parallel(const RetArgs &a, hipStream_t st) {
   if (a.dk == 256 && a.dv == 512) return run_qblocks<256, 512>(a, geo, true, nullptr, st, false);
   return hipErrorNotSupported;
 }
+
+int resident_chunk_max(int dk) { return kres_of(dk) * BT; }
 
 hipError_t launch_mfma_chunkwise_out(const RetArgs &a, const ChunkPlan &p, void *ws, hipStream_t st) {
   char *w = (char *)ws;

@@ -36,7 +36,8 @@ def test_backward_fp32(L, chunk, pos0, rot):
 @pytest.mark.parametrize("dk,dv,L,chunk,rot,pos0", [(128, 256, 300, 64, True, 3), (128, 256, 513, 256, True, 3),
                                                      (64, 128, 200, 100, True, 3), (128, 128, 260, 128, True, 3),
                                                      (64, 128, 130, 64, False, 0),
-                                                     (128, 256, 200, 64, True, 100000)])
+                                                     (128, 256, 200, 64, True, 100000),
+                                                     (128, 256, 389, 128, True, 5), (128, 256, 1100, 256, False, 0)])
 def test_backward_bf16(dk, dv, L, chunk, rot, pos0):
     """bf16 inputs on the MFMA kernels, which rotate on load (value rows at their
     own positions, reversed queries and keys by -theta): with and without

@@ -18,7 +18,7 @@ from workloads import multiscale_gamma, randn, rotation_theta
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-PAIRS = [(64, 128), (128, 128), (128, 256), (256, 256), (256, 512)]
+PAIRS = [(64, 128), (128, 128), (128, 256), (256, 128), (256, 256), (256, 512)]
 
 
 def _qkv(B, H, L, dk, dv, seed):
