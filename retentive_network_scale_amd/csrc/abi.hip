@@ -140,12 +140,25 @@ size_t chunk_ws_bytes(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_
 // Backward workspace: rotated / reversed copies of the inputs (input dtype), the
 // three fp32 retention outputs and one chunkwise workspace shared by the three
 // retention calls (they run one after the other on the stream).
-// Chunk of the backward's inner retentions whose queries and keys are dv wide:
-// the longest chunk dividing the caller's whose keys stay resident in LDS
-// (segment boundaries, multiples of the caller's chunk, are kept).
-int bwd_wide_chunk(int dv, int chunk) {
-  const int r = resident_chunk_max(dv);
-  return chunk > r && chunk % r == 0 ? r : chunk;
+// Chunks the backward's inner retentions walk their segments in: divisors of the
+// caller's chunk, so the segment boundaries (multiples of the caller's chunk)
+// stay where the caller's chunk puts them.  narrow: the dv sum, queries and keys
+// dk wide; wide: the dk~ and dq~ sums, queries and keys dv wide, at most the
+// longest chunk whose keys stay resident in LDS.  wide divides narrow.  A chunk
+// only blocks the computation (the sums are the same up to rounding); 64-token
+// chunks cost the least here: the intra-chunk work shrinks with the chunk, the
+// state work does not grow.
+constexpr int BWD_NARROW_CHUNK = 64, BWD_WIDE_CHUNK = 64;
+struct BwdChunks {
+  int narrow, wide;
+};
+BwdChunks bwd_chunks(int dv, int chunk) {
+  auto part = [chunk](int t) { return chunk > t && chunk % t == 0 ? t : chunk; };
+  BwdChunks c;
+  c.narrow = part(BWD_NARROW_CHUNK);
+  c.wide = part(std::min(BWD_WIDE_CHUNK, resident_chunk_max(dv)));
+  if (c.narrow % c.wide) c.wide = c.narrow;
+  return c;
 }
 
 struct BwdPlan {
@@ -175,7 +188,9 @@ BwdPlan bwd_plan(int B, int H, int L, int dk, int dv, int chunk, ret_dtype_t in_
   off += al(R * dv * 4);
   p.cws = off;
   p.cws_bytes = std::max(chunk_ws_bytes(B, H, L, dv, dk, chunk, in_dtype), chunk_ws_bytes(B, H, L, dk, dv, chunk, in_dtype));
-  p.cws_bytes = std::max(p.cws_bytes, chunk_ws_bytes(B, H, L, dv, dk, bwd_wide_chunk(dv, chunk), in_dtype));
+  const BwdChunks bc = bwd_chunks(dv, chunk);
+  p.cws_bytes = std::max({p.cws_bytes, chunk_ws_bytes(B, H, L, dk, dv, bc.narrow, in_dtype),
+                          chunk_ws_bytes(B, H, L, dv, dk, bc.wide, in_dtype)});
   off += al(p.cws_bytes);
   p.total = off;
   return p;
@@ -442,15 +457,16 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
     // Without rotation the sums read k and q themselves.
     const void *kr = rot ? (const void *)(ws + p.kr) : k, *qr = rot ? (const void *)(ws + p.qrev) : q;
     e = rot ? launch_bwd_prep2(k, ws + p.kr, q, ws + p.qrev, rows, L, dk, pos0, bf, th, st) : hipSuccess;
+    const BwdChunks bc = bwd_chunks(dv, chunk);
+    const int cw = bc.wide;
     if (e != hipSuccess ||
-        (e = bwd_retention(kr, qr, d_o, dv_out, dvr, B, H, L, dk, dv, chunk, gamma, nullptr, pos0, false, true,
+        (e = bwd_retention(kr, qr, d_o, dv_out, dvr, B, H, L, dk, dv, bc.narrow, gamma, nullptr, pos0, false, true,
                            in_dtype, out_dtype, cws, st, true)) != hipSuccess)
       return hip_status(e);
-    const int cw = bwd_wide_chunk(dv, chunk);
     {
-      // same segments as the dv sum's states, walked in chunks of cw
-      ChunkPlan pl = chunk_plan(B, H, L, dv, dk, chunk);
-      pl.seg_chunks *= chunk / cw;
+      // the dv sum's segments, walked in chunks of cw
+      ChunkPlan pl = chunk_plan(B, H, L, dk, dv, bc.narrow);
+      pl.seg_chunks *= bc.narrow / cw;
       RetArgs a = make_args(v, d_o, qr, dk_out, B, H, L, dv, dk, cw, gamma, nullptr, pos0, -1.0f, in_dtype,
                             out_dtype);
       a.in_rev = 1;
