@@ -171,8 +171,9 @@ def bench_chunkwise_bwd(steps, warmup):
     return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3, **spread,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": _read_traffic("chunkwise_bwd"),
-                         "kernel": "retention_chunkwise_bwd call: rotate/reverse passes, three chunkwise "
-                                   "retentions writing the gradients through an un-rotating, reversing epilogue",
+                         "kernel": "retention_chunkwise_bwd call: one rotation pass, three chunkwise retentions "
+                                   "(64-token chunks inside the chunk-256 segments) writing the gradients through "
+                                   "an un-rotating, reversing epilogue",
                          "algorithmic_bytes_per_call": bytes_alg}}
 
 

@@ -53,6 +53,24 @@ def test_backward_bf16(dk, dv, L, chunk, rot, pos0):
         _tol.assert_bf16(a, b, slice_dims=2, what=f"d{name}")
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 128), (128, 256)])
+@pytest.mark.parametrize("chunk", [192, 256])
+def test_backward_chunks_split_inside_segments(dk, dv, chunk):
+    """A caller's chunk that is a multiple of 64 is walked in 64-token chunks inside
+    the caller's segments; the dk sum then reads the dv sum's segment states.
+    Two sequences, three heads, a ragged length spanning several segments, bf16
+    with rotation, against the oracle's gradients."""
+    B, H, L = 2, 3, 450
+    q, k, v, do = _inputs(B, H, L, dk, dv, 1500 + dk + dv + chunk, torch.bfloat16)
+    g, th = multiscale_gamma(H), rotation_theta(dk)
+    got = rn.retention_chunkwise_bwd(*(t.to(DEV) for t in (q, k, v, do)), g, chunk, th, pos0=9,
+                                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.backward(q, k, v, do, g, th, 9)
+    for name, a, b in zip("qkv", got, ref):
+        _tol.assert_bf16(a, b, slice_dims=2, what=f"d{name} dk={dk} dv={dv} chunk={chunk}")
+
+
 def test_backward_32k_sampled_rows():
     """The long-context workload (B1 H8 L32768 dk128 dv256, chunk 256) with a seeded
     output gradient: ten sampled rows of dq, dk and dv in each of three heads (the
