@@ -170,8 +170,11 @@ ret_status_t retention_recurrent_step(const void *q, const void *k, const void *
  *   dq_n = R_n^T sum_{m<=n} a_nm (dO_n . v_m) k~_m
  *   dk_m = R_m^T sum_{n>=m} a_nm (dO_n . v_m) q~_n
  * (R_n: the rotation at position pos0 + n).  The initial state is zero.
- * Each sum is itself a retention and runs on the chunkwise kernels with the given
- * chunk (the two anti-causal sums on the token-reversed sequence).
+ * Each sum is itself a retention and runs on the chunkwise kernels (the two
+ * anti-causal sums on the token-reversed sequence), in segments whose bounds are
+ * multiples of the given chunk; on the MFMA kernels a chunk that is a multiple of
+ * 64 is walked in 64-token pieces inside them (a chunk only blocks the sums: the
+ * gradients are the same up to rounding).
  *   q, k : [B,H,L,dk]   v, d_o : [B,H,L,dv]   (in_dtype)
  *   dq, dk_out : [B,H,L,dk]   dv_out : [B,H,L,dv]   (out_dtype)
  * UNSUPPORTED unless dk and dv are multiples of 8 and dv <= RETENTION_MAX_DK.  Gradients must not

@@ -1070,7 +1070,7 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
 // last query block runs (it visits them all), so the cross terms of the
 // earlier blocks see S_c.  Global loads of the next visit are in flight
 // during the current one.
-// RES (chunks of at most KRES key blocks, no hi/lo split): the chunk's rotated
+// RES (chunks of at most kres_of(DK) key blocks, no hi/lo split): the chunk's rotated
 // keys stay in LDS, so each key block is fetched and rotated once, at its
 // diagonal visit; the update's zeta-scaled transposed copy of an earlier block
 // is rebuilt from LDS.
