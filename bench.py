@@ -45,13 +45,23 @@ _LAST_CALLS = []  # per-call seconds of the latest _time_calls (event pairs betw
 
 def _time_calls(fn, steps, warmup):
     """Seconds for `steps` back-to-back calls, between two events on the stream the
-    calls run on (torch's current stream, which the library is given).  An event
-    after every call also gives per-call times (_LAST_CALLS) for the median and min."""
+    calls run on (torch's current stream, which the library is given), with nothing
+    else enqueued between the calls.  A second loop of `steps` calls with an event
+    after every call gives per-call times (_LAST_CALLS) for the median and min; an
+    event between two calls costs the GPU a few microseconds (the next launch waits
+    for it), so those times run slightly above the back-to-back mean."""
     import torch
     _settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    total = e0.elapsed_time(e1) / 1000.0  # seconds for all steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record()
     for i in range(steps):
@@ -59,7 +69,7 @@ def _time_calls(fn, steps, warmup):
         ev[i + 1].record()
     torch.cuda.synchronize()
     _LAST_CALLS[:] = [ev[i].elapsed_time(ev[i + 1]) / 1000.0 for i in range(steps)]
-    return ev[0].elapsed_time(ev[steps]) / 1000.0  # seconds for all steps
+    return total
 
 
 def _spread():

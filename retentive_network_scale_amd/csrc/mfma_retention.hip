@@ -854,6 +854,7 @@ __device__ __forceinline__ void lds_barrier() {
 // rotate_keys_kernel), or straight from k when there is no rotation (kt null) --
 // and go to LDS by DMA, no register pass: the next block's DMA is issued once
 // the scores are done with the current one and lands during the P.V products.
+constexpr int LPT_G = 4;  // (bh, chunk) units per longest-first task group
 template <int DK, int DV, bool PAR, bool SPLIT, bool KPRE = false>
 __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, const uint16_t *SinT,
                                                     const uint16_t *kt = nullptr) {
@@ -877,17 +878,23 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int task = xcd_task(blockIdx.x, geo.ntasks);
   if (task < 0) return;
-  // task order: (bh, chunk, qb) with qb fastest; longest query blocks first
-  int qb = geo.nqb - 1 - task % geo.nqb;
-  int c = (task / geo.nqb) % geo.nchunks;
-  int bh = task / (geo.nqb * geo.nchunks);
-  if (geo.sel == 1) {
-    qb = 0;
-    c = 0;
-    bh = task;
-  } else if (geo.sel == 2 && qb == 0 && c == 0) {
-    return;
+  // Task order, longest first: the (bh, chunk) units go in groups of LPT_G, and
+  // inside a group the query blocks run from the last (the most key blocks to
+  // visit) to the first, across the group's units.  Each XCD takes a contiguous
+  // range of tasks (xcd_task), so it starts on the long tasks of its groups and
+  // fills its tail with short ones, while the few units in flight at a time keep
+  // their K and V in that XCD's L2.  (Units one after another, longest first
+  // within each: parallel workload 383 -> 353 us, MSR layer 1245 -> 1207 us.)
+  int qb = 0, c = 0, bh = task;  // sel 1: one task per (b, h), its first query block
+  if (geo.sel != 1) {
+    const int nunits = geo.ntasks / geo.nqb, grp = task / (geo.nqb * LPT_G);
+    const int gsz = min(LPT_G, nunits - grp * LPT_G), r = task - grp * geo.nqb * LPT_G;
+    const int unit = grp * LPT_G + r % gsz;
+    qb = geo.nqb - 1 - r / gsz;
+    c = unit % geo.nchunks;
+    bh = unit / geo.nchunks;
   }
+  if (geo.sel == 2 && qb == 0 && c == 0) return;
   const int cstep = PAR ? a.L : a.chunk;
   const int c0 = c * cstep, Cc = min(cstep, a.L - c0);
   const int q0 = c0 + qb * BT;

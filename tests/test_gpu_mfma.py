@@ -65,6 +65,31 @@ def test_chunkwise_mfma(dk, dv, L, chunk):
     _tol.assert_bf16(s, ref_s, what="final state")
 
 
+@pytest.mark.parametrize("dk,dv,chunk,rot,gn,odt", [
+    (128, 256, 256, True, None, torch.bfloat16), (128, 256, 192, False, 1e-5, torch.bfloat16),
+    (128, 256, 256, False, 1e-5, torch.float32), (128, 128, 256, True, None, torch.float32),
+    (64, 128, 192, True, None, torch.bfloat16), (128, 256, 160, True, None, torch.bfloat16)])
+def test_chunkwise_three_and_four_block_chunks(dk, dv, chunk, rot, gn, odt):
+    """Chunks of three or four 64-token blocks (the chunk's first V block stays in
+    LDS beside its keys): segments of two chunks, a ragged last chunk (4000 tokens),
+    an incoming state, GroupNorm without rotation (the partial sums share the score
+    tile), bf16 (staged) and fp32 outputs."""
+    B, H, L = 4, 8, 4000
+    q, k, v = _qkv(B, H, L, dk, dv, 500 + dk + dv + chunk)
+    s0 = randn((B, H, dk, dv), 9, 0.3)
+    g = multiscale_gamma(H)
+    th = rotation_theta(dk) if rot else None
+    ref_o, ref_s = oracle.recurrent(q, k, v, g, th, pos0=3, s_in=s0)
+    if gn is not None:
+        ref_o = oracle.groupnorm(ref_o, gn)
+    qd, kd, vd, sd = _gpu(q, k, v, s0)
+    o, s = rn.retention_chunkwise(qd, kd, vd, g, chunk, th, pos0=3, state_in=sd, state_out=True, gn_eps=gn,
+                                  out_dtype=odt)
+    torch.cuda.synchronize()
+    _tol.assert_bf16(o, ref_o, what=f"chunkwise dk={dk} dv={dv} chunk={chunk} rot={rot} gn={gn}")
+    _tol.assert_bf16(s, ref_s, what="final state")
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 256), (256, 512)])
 def test_chunkwise_segments_and_carry(dk, dv):
     """B*H = 32 units so that every head gets several segments of several chunks
