@@ -178,13 +178,34 @@ def bench_chunkwise_bwd(steps, warmup):
     spread = _spread()
     bytes_alg = _alg_bytes_bwd()
     achieved = bytes_alg / per_call / 1e9
+    # The same gradients with the forward call's segment states handed over (as a
+    # training step keeps them): the forward runs once, untimed, into its
+    # workspace; then the backward alone, and forward + backward as one step.
+    fo = torch.empty_like(v)
+    fws = torch.empty(rn.retention_chunkwise_workspace_bytes(wl.B, wl.H, wl.L, wl.dk, wl.dv, wl.chunk),
+                      dtype=torch.uint8, device="cuda")
+    rn.retention_chunkwise(q, k, v, g, wl.chunk, th, out=fo, workspace=fws)
+    t_s = _time_calls(lambda: rn.retention_chunkwise_bwd(q, k, v, do, g, wl.chunk, th, out=outs, workspace=ws,
+                                                         fwd_workspace=fws), steps, warmup)
+    saved = {"ms_per_step": t_s / steps * 1e3, "tokens_per_s": wl.B * wl.L * steps / t_s, **_spread(),
+             "hbm_frac": bytes_alg / (t_s / steps) / 1e9 / HBM_PEAK_GBS,
+             "what": "retention_chunkwise_bwd_saved: the dq sum reads the forward call's segment states "
+                     "(no state pass or scan of its own)"}
+
+    def train_step():
+        rn.retention_chunkwise(q, k, v, g, wl.chunk, th, out=fo, workspace=fws)
+        rn.retention_chunkwise_bwd(q, k, v, do, g, wl.chunk, th, out=outs, workspace=ws, fwd_workspace=fws)
+    t_t = _time_calls(train_step, steps, warmup)
+    train = {"ms_per_step": t_t / steps * 1e3, "tokens_per_s": wl.B * wl.L * steps / t_t, **_spread(),
+             "what": "forward (retention_chunkwise, bf16 out) then the backward with its segment states"}
     return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3, **spread,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": _read_traffic("chunkwise_bwd"),
                          "kernel": "retention_chunkwise_bwd call: one rotation pass, three chunkwise retentions "
                                    "(64-token chunks inside the chunk-256 segments) writing the gradients through "
                                    "an un-rotating, reversing epilogue",
-                         "algorithmic_bytes_per_call": bytes_alg}}
+                         "algorithmic_bytes_per_call": bytes_alg},
+            "with_forward_states": saved, "forward_plus_backward": train}
 
 
 SWEEP_CHUNKS = (64, 128, 256, 512, 1024, 2048)

@@ -190,6 +190,32 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
                                      void *hip_stream);
 
 /*
+ * The same gradients, reusing the segment states of the forward call
+ * (retention_chunkwise, "Retentive Network" paper summary, Sec. 2.1 (3): the state
+ * carried across chunks).  The dq sum carries sum_{m<=n} gamma^(n-m) v_m^T k~_m,
+ * the transpose of the forward's state sum_{m<=n} gamma^(n-m) k~_m^T v_m, so with
+ * the forward's states it needs no state pass of its own: a training step keeps
+ * the forward's workspace (as it keeps activations) and hands it over here.
+ *   fwd_workspace : the workspace of a retention_chunkwise call with the same q, k,
+ *                   v (bf16), B, H, L, dk, dv, chunk, gamma, theta and pos0 and no
+ *                   state_in, unchanged since (its first part holds the fp32 states
+ *                   entering each segment, written by that call); read only.
+ *                   Its content is not checked: other contents give other dq.
+ *   fwd_workspace_bytes : its size (at least the forward's segment states).
+ * Where the states are not usable (inputs on the vector path, or a forward plan
+ * whose segments do not take the states in registers) the dq sum computes its own,
+ * as retention_chunkwise_bwd does.  INVALID_ARG for a NULL or unaligned
+ * fwd_workspace or one that overlaps a gradient; WORKSPACE if it is too small.
+ */
+ret_status_t retention_chunkwise_bwd_saved(const void *q, const void *k, const void *v,
+                                           const void *d_o, void *dq, void *dk_out, void *dv_out,
+                                           int B, int H, int L, int dk, int dv, int chunk,
+                                           const float *gamma, const float *theta, long long pos0,
+                                           ret_dtype_t in_dtype, ret_dtype_t out_dtype,
+                                           const void *fwd_workspace, size_t fwd_workspace_bytes,
+                                           void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * Gated multi-scale retention layer (Sec. 2.2), bf16 in and out:
  *   Q = X W_Q, K = X W_K, V = X W_V (head h = column block h of width dk / dv)
  *   head_h = chunkwise retention of (Q_h, K_h, V_h) with gamma_h, theta, pos0

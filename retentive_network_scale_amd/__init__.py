@@ -19,7 +19,8 @@ __all__ = [
     "retention_chunkwise_workspace_bytes", "retention_chunkwise_noalloc", "retention_recurrent_step",
     "msr_layer_fwd",
     "msr_layer_fwd_workspace_bytes", "msr_layer_step", "msr_layer_step_workspace_bytes",
-    "retention_chunkwise_bwd", "retention_chunkwise_bwd_workspace_bytes", "retnet_block_fwd",
+    "retention_chunkwise_bwd", "retention_chunkwise_bwd_workspace_bytes",
+    "retnet_block_fwd",
     "retnet_block_fwd_workspace_bytes", "LIB_PATH",
     "EXPORTED_SYMBOLS",
 ]
@@ -48,6 +49,8 @@ _SIGS = {
     "retention_chunkwise_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "retention_chunkwise_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _fp, _fp, _ll,
                                      _i, _i, _vp, _sz, _vp]),
+    "retention_chunkwise_bwd_saved": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _fp, _fp,
+                                           _ll, _i, _i, _vp, _sz, _vp, _sz, _vp]),
     "msr_layer_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "msr_layer_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _fp, _fp, _ll,
                            _f, _vp, _sz, _vp]),
@@ -286,9 +289,12 @@ def retention_chunkwise_bwd_workspace_bytes(B, H, L, dk, dv, chunk, in_dtype=tor
 
 
 def retention_chunkwise_bwd(q, k, v, d_o, gamma, chunk, theta=None, pos0=0, out_dtype=None, out=None,
-                            workspace=None, stream=None):
+                            workspace=None, stream=None, fwd_workspace=None):
     """Gradients (dq, dk, dv) of chunkwise retention (no GroupNorm, zero initial
-    state) for the output gradient d_o.  q, k [B,H,L,dk]; v, d_o [B,H,L,dv]."""
+    state) for the output gradient d_o.  q, k [B,H,L,dk]; v, d_o [B,H,L,dv].
+    fwd_workspace: the workspace of the forward retention_chunkwise call on the
+    same inputs (no state_in), whose segment states the dq sum then reuses
+    (retention_chunkwise_bwd_saved)."""
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     od = out_dtype or q.dtype
@@ -301,11 +307,14 @@ def retention_chunkwise_bwd(q, k, v, d_o, gamma, chunk, theta=None, pos0=0, out_
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     g, gp = _host_f32(gamma, H, "gamma")
     th, thp = _host_f32(theta, dk // 2, "theta")
-    _check(lib().retention_chunkwise_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(d_o, "d_o"),
-                                         _dev(out[0], "dq"), _dev(out[1], "dk"), _dev(out[2], "dv"), B, H, L, dk,
-                                         dv, int(chunk), gp, thp, int(pos0), _dtc(q.dtype), _dtc(od),
-                                         _dev(workspace, "workspace"),
-                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+    common = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(d_o, "d_o"), _dev(out[0], "dq"), _dev(out[1], "dk"),
+              _dev(out[2], "dv"), B, H, L, dk, dv, int(chunk), gp, thp, int(pos0), _dtc(q.dtype), _dtc(od))
+    tail = (_dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    if fwd_workspace is None:
+        _check(lib().retention_chunkwise_bwd(*common, *tail))
+    else:
+        _check(lib().retention_chunkwise_bwd_saved(*common, _dev(fwd_workspace, "fwd_workspace"),
+                                                   fwd_workspace.numel() * fwd_workspace.element_size(), *tail))
     return out
 
 

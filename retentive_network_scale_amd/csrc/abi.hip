@@ -405,11 +405,13 @@ size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int L, int dk, int 
   return bwd_plan(B, H, L, dk, dv, chunk, in_dtype).total;
 }
 
-ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v, const void *d_o, void *dq,
-                                     void *dk_out, void *dv_out, int B, int H, int L, int dk, int dv, int chunk,
-                                     const float *gamma, const float *theta, long long pos0, ret_dtype_t in_dtype,
-                                     ret_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
-                                     void *hip_stream) {
+// The backward; fwd_ws (optional) is the workspace of the forward call whose
+// segment states the dq~ sum reads instead of computing its own.
+static ret_status_t chunkwise_bwd(const void *q, const void *k, const void *v, const void *d_o, void *dq,
+                                  void *dk_out, void *dv_out, int B, int H, int L, int dk, int dv, int chunk,
+                                  const float *gamma, const float *theta, long long pos0, ret_dtype_t in_dtype,
+                                  ret_dtype_t out_dtype, const void *fwd_ws, size_t fwd_ws_bytes, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream) {
   ret_status_t s = check_common(B, H, L, dk, dv, gamma, theta, pos0, -1.0f, in_dtype, out_dtype);
   if (s != RET_OK) return s;
   if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk=%d must be positive", chunk);
@@ -419,10 +421,15 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
     return fail(RET_ERR_UNSUPPORTED, "the backward needs dv <= %d", RETENTION_MAX_DK);
   if (L == 0) return ok();
   if (!q || !k || !v || !d_o || !dq || !dk_out || !dv_out) return fail(RET_ERR_INVALID_ARG, "NULL tensor pointer");
-  const void *ptrs[] = {q, k, v, d_o, dq, dk_out, dv_out, workspace};
+  const void *ptrs[] = {q, k, v, d_o, dq, dk_out, dv_out, workspace, fwd_ws};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return fail(RET_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   const BwdPlan p = bwd_plan(B, H, L, dk, dv, chunk, in_dtype);
+  // the forward's segment states: fp32 [B*H][nseg][dk][dv] at the start of its workspace
+  const ChunkPlan fwd_plan = chunk_plan(B, H, L, dk, dv, chunk);
+  if (fwd_ws && fwd_ws_bytes < fwd_plan.seg_bytes)
+    return fail(RET_ERR_WORKSPACE, "forward workspace of %zu bytes needed, %zu given", fwd_plan.seg_bytes,
+                fwd_ws_bytes);
   if (!workspace || workspace_bytes < p.total)
     return fail(RET_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace_bytes);
   const size_t R = (size_t)B * H * L;
@@ -431,7 +438,8 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
   const struct {
     const void *p;
     size_t n;
-  } ins[] = {{q, nqk}, {k, nqk}, {v, nv}, {d_o, nv}, {workspace, p.total}}, outs[] = {{dq, oqk}, {dk_out, oqk}, {dv_out, ov}};
+  } ins[] = {{q, nqk}, {k, nqk}, {v, nv}, {d_o, nv}, {workspace, p.total}, {fwd_ws, fwd_ws ? fwd_plan.seg_bytes : 0}},
+    outs[] = {{dq, oqk}, {dk_out, oqk}, {dv_out, ov}};
   for (const auto &o : outs) {
     for (const auto &i : ins)
       if (overlap(o.p, o.n, i.p, i.n)) return fail(RET_ERR_INVALID_ARG, "a gradient overlaps an input or the workspace");
@@ -477,6 +485,22 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
       a.state_t = 1;
       if ((e = launch_mfma_chunkwise_out(a, pl, cws, st)) != hipSuccess) return hip_status(e);
     }
+    if (fwd_ws && fwd_plan.in_regs && chunk % cw == 0) {
+      // The dq~ sum's states, sums over earlier tokens of v^T k~, are the
+      // transposes of the forward's k~^T v over the same segments with the same
+      // decay: its output pass reads the states entering each segment from the
+      // forward call's workspace, transposed, with no state pass or scan.
+      ChunkPlan pl = fwd_plan;
+      pl.seg_chunks *= chunk / cw;
+      RetArgs a = make_args(d_o, v, kr, dq, B, H, L, dv, dk, cw, gamma, nullptr, pos0, -1.0f, in_dtype, out_dtype);
+      a.out_rot = rot;
+      if (rot)
+        for (int i = 0; i < dk / 2; ++i) a.theta[i] = theta[i];
+      a.state_t = 1;
+      if ((e = launch_mfma_chunkwise_out(a, pl, const_cast<void *>(fwd_ws), st)) != hipSuccess)
+        return hip_status(e);
+      return ok();
+    }
     if ((e = bwd_retention(d_o, v, kr, dq, dqr, B, H, L, dv, dk, cw, gamma, theta, pos0, true, false, in_dtype,
                            out_dtype, cws, st)) != hipSuccess)
       return hip_status(e);
@@ -496,6 +520,26 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
                          pos0, false, true, in_dtype, out_dtype, cws, st)) != hipSuccess)
     return hip_status(e);
   return ok();
+}
+
+ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v, const void *d_o, void *dq,
+                                     void *dk_out, void *dv_out, int B, int H, int L, int dk, int dv, int chunk,
+                                     const float *gamma, const float *theta, long long pos0, ret_dtype_t in_dtype,
+                                     ret_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
+                                     void *hip_stream) {
+  return chunkwise_bwd(q, k, v, d_o, dq, dk_out, dv_out, B, H, L, dk, dv, chunk, gamma, theta, pos0, in_dtype,
+                       out_dtype, nullptr, 0, workspace, workspace_bytes, hip_stream);
+}
+
+ret_status_t retention_chunkwise_bwd_saved(const void *q, const void *k, const void *v, const void *d_o, void *dq,
+                                           void *dk_out, void *dv_out, int B, int H, int L, int dk, int dv,
+                                           int chunk, const float *gamma, const float *theta, long long pos0,
+                                           ret_dtype_t in_dtype, ret_dtype_t out_dtype, const void *fwd_workspace,
+                                           size_t fwd_workspace_bytes, void *workspace, size_t workspace_bytes,
+                                           void *hip_stream) {
+  if (!fwd_workspace) return fail(RET_ERR_INVALID_ARG, "NULL forward workspace");
+  return chunkwise_bwd(q, k, v, d_o, dq, dk_out, dv_out, B, H, L, dk, dv, chunk, gamma, theta, pos0, in_dtype,
+                       out_dtype, fwd_workspace, fwd_workspace_bytes, workspace, workspace_bytes, hip_stream);
 }
 
 ret_status_t retention_recurrent_step(const void *q, const void *k, const void *v, float *state,

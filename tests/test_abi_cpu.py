@@ -170,6 +170,27 @@ def test_backward_rejects_and_workspace():
     assert call(dq=FAKE) == INVALID  # a gradient overlapping an input
 
 
+def test_backward_with_forward_states_rejects():
+    """The backward that reuses a forward call's segment states validates that
+    workspace too: NULL or misaligned, too small for the forward's states, or
+    overlapping a gradient."""
+    L = rn.lib()
+    g = _f([0.9] * 2)
+    B, H, Ln, dk, dv, chunk = 1, 2, 4096, 128, 256, 256
+    need = L.retention_chunkwise_bwd_workspace_bytes(B, H, Ln, dk, dv, chunk, BF16)
+    fwd_need = L.retention_chunkwise_workspace_bytes(B, H, Ln, dk, dv, chunk, BF16)
+    DQ, DK_, DV_, WS, FW = (ctypes.c_void_p(a << 32) for a in (1, 2, 3, 4, 5))
+
+    def call(fw=FW, fwb=fwd_need, dq=DQ):
+        return L.retention_chunkwise_bwd_saved(FAKE, FAKE2, FAKE3, FAKE4, dq, DK_, DV_, B, H, Ln, dk, dv, chunk, g,
+                                               None, 0, BF16, BF16, fw, fwb, WS, need, None)
+    assert call(fw=ctypes.c_void_p(0)) == INVALID
+    assert call(fw=ctypes.c_void_p((5 << 32) + 8)) == INVALID  # not 16-byte aligned
+    assert call(fwb=fwd_need // 2) == WORKSPACE
+    assert b"forward workspace" in L.retention_last_error()
+    assert call(dq=FW) == INVALID  # a gradient overlapping the forward's states
+
+
 def test_block_rejects():
     L = rn.lib()
     g = _f([0.9] * 2)

@@ -91,3 +91,53 @@ def test_backward_32k_sampled_rows():
         ref = oracle.backward_rows(qn, kn, vn, don, g, name, idx, th).reshape(len(heads), per, -1)
         gotr = np.stack([t[b, h, n].float().cpu().numpy() for b, h, n in idx]).reshape(len(heads), per, -1)
         _tol.assert_bf16(gotr, ref, slice_dims=1, what=f"d{name} sampled rows, per head")
+
+
+@pytest.mark.parametrize("dk,dv,B,H,L,chunk,rot,pos0", [(128, 256, 1, 4, 513, 256, True, 3),
+                                                         (128, 256, 2, 8, 2000, 192, True, 7),
+                                                         (128, 256, 4, 8, 4000, 128, True, 0),
+                                                         (64, 128, 2, 8, 1500, 128, False, 0),
+                                                         (128, 128, 1, 4, 700, 64, True, 11)])
+def test_backward_with_forward_states(dk, dv, B, H, L, chunk, rot, pos0):
+    """The backward that reuses the forward call's segment states for the dq sum
+    (retention_chunkwise_bwd_saved): the forward runs first on the same inputs and
+    its workspace is handed over.  Gradients against the oracle, and against the
+    self-contained backward.  Shapes give one and several segments per head, a
+    ragged last chunk, several chunks per segment and a chunk split into 64-token
+    pieces inside segments.  The reference is the oracle's recurrent adjoint."""
+    q, k, v, do = _inputs(B, H, L, dk, dv, 1300 + dk + L, torch.bfloat16)
+    g, th = multiscale_gamma(H), (rotation_theta(dk) if rot else None)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    fws = torch.empty(rn.retention_chunkwise_workspace_bytes(B, H, L, dk, dv, chunk), dtype=torch.uint8, device=DEV)
+    rn.retention_chunkwise(qd, kd, vd, g, chunk, th, pos0=pos0, workspace=fws)
+    got = rn.retention_chunkwise_bwd(qd, kd, vd, dod, g, chunk, th, pos0=pos0, out_dtype=torch.float32,
+                                     fwd_workspace=fws)
+    own = rn.retention_chunkwise_bwd(qd, kd, vd, dod, g, chunk, th, pos0=pos0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.backward_recurrent(q, k, v, do, g, th, pos0)
+    for name, a, b, c in zip("qkv", got, ref, own):
+        _tol.assert_bf16(a, b, slice_dims=2, what=f"d{name} with forward states")
+        _tol.assert_bf16(a, c.double().cpu().numpy(), slice_dims=2, what=f"d{name} vs own states")
+
+
+def test_backward_32k_with_forward_states_sampled_rows():
+    """The long-context workload's backward with the forward's states: ten sampled
+    rows of dq (the sum that reads them) in each of three heads, per head."""
+    wl = CHUNKWISE_32K
+    q, k, v = wl.qkv()
+    do = randn((wl.B, wl.H, wl.L, wl.dv), 3009, 1.0, torch.bfloat16)
+    g, th = wl.gamma(), wl.theta()
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    fws = torch.empty(rn.retention_chunkwise_workspace_bytes(wl.B, wl.H, wl.L, wl.dk, wl.dv, wl.chunk),
+                      dtype=torch.uint8, device=DEV)
+    rn.retention_chunkwise(qd, kd, vd, g, wl.chunk, th, workspace=fws)
+    got = rn.retention_chunkwise_bwd(qd, kd, vd, dod, g, wl.chunk, th, fwd_workspace=fws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    heads, per = (0, 3, 7), 10
+    fixed = [0, 1023, 1024, 20000, wl.L - 1]
+    idx = [(0, h, n) for h in heads for n in fixed + [int(x) for x in rng.integers(wl.L, size=per - len(fixed))]]
+    qn, kn, vn, don = (oracle.as_f64(t) for t in (q, k, v, do))
+    ref = oracle.backward_rows(qn, kn, vn, don, g, "q", idx, th).reshape(len(heads), per, -1)
+    gotr = np.stack([got[0][b, h, n].float().cpu().numpy() for b, h, n in idx]).reshape(len(heads), per, -1)
+    _tol.assert_bf16(gotr, ref, slice_dims=1, what="dq sampled rows with forward states, per head")
