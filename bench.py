@@ -160,9 +160,12 @@ def bench_chunkwise(steps, warmup):
     }
 
 
-def bench_chunkwise_bwd(steps, warmup):
+def bench_chunkwise_bwd(steps, warmup, with_saved=True):
     """Gradients of retention (dq, dk, dv) on the long-context workload (B1 H8
-    L32768 dk128 dv256, chunk 256, bf16 in and out) for a seeded output gradient."""
+    L32768 dk128 dv256, chunk 256, bf16 in and out) for a seeded output gradient.
+    with_saved: also the backward on the forward call's segment states, and the
+    forward + backward step (left out of the counter runs, which count the
+    self-contained backward's calls)."""
     import torch
     import retentive_network_scale_amd as rn
     from workloads import CHUNKWISE_32K as wl, randn
@@ -178,6 +181,15 @@ def bench_chunkwise_bwd(steps, warmup):
     spread = _spread()
     bytes_alg = _alg_bytes_bwd()
     achieved = bytes_alg / per_call / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": _read_traffic("chunkwise_bwd"),
+            "kernel": "retention_chunkwise_bwd call: one rotation pass, three chunkwise retentions "
+                      "(64-token chunks inside the chunk-256 segments) writing the gradients through "
+                      "an un-rotating, reversing epilogue",
+            "algorithmic_bytes_per_call": bytes_alg}
+    res = {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3, **spread, "roofline": roof}
+    if not with_saved:
+        return res
     # The same gradients with the forward call's segment states handed over (as a
     # training step keeps them): the forward runs once, untimed, into its
     # workspace; then the backward alone, and forward + backward as one step.
@@ -198,14 +210,7 @@ def bench_chunkwise_bwd(steps, warmup):
     t_t = _time_calls(train_step, steps, warmup)
     train = {"ms_per_step": t_t / steps * 1e3, "tokens_per_s": wl.B * wl.L * steps / t_t, **_spread(),
              "what": "forward (retention_chunkwise, bf16 out) then the backward with its segment states"}
-    return {"tokens_per_s": wl.B * wl.L / per_call, "ms_per_step": per_call * 1e3, **spread,
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": _read_traffic("chunkwise_bwd"),
-                         "kernel": "retention_chunkwise_bwd call: one rotation pass, three chunkwise retentions "
-                                   "(64-token chunks inside the chunk-256 segments) writing the gradients through "
-                                   "an un-rotating, reversing epilogue",
-                         "algorithmic_bytes_per_call": bytes_alg},
-            "with_forward_states": saved, "forward_plus_backward": train}
+    return {**res, "with_forward_states": saved, "forward_plus_backward": train}
 
 
 SWEEP_CHUNKS = (64, 128, 256, 512, 1024, 2048)
@@ -764,7 +769,7 @@ def main():
         res = {"decode": lambda: bench_decode(), "parallel": lambda: bench_parallel(args.steps, args.warmup),
                "msr": lambda: bench_msr(args.steps, args.warmup),
                "msr_decode": lambda: bench_msr_decode(),
-               "bwd": lambda: bench_chunkwise_bwd(args.steps, args.warmup),
+               "bwd": lambda: bench_chunkwise_bwd(args.steps, args.warmup, with_saved=False),
                "block": lambda: bench_block(args.steps, args.warmup),
                "sweep": lambda: {"chunk_sweep": bench_chunk_sweep(args.steps, args.warmup)}}[args.only]()
         print(json.dumps({"workload": args.only, **res}), flush=True)
