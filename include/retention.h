@@ -205,7 +205,8 @@ ret_status_t retention_chunkwise_bwd(const void *q, const void *k, const void *v
  * Where the states are not usable (inputs on the vector path, or a forward plan
  * whose segments do not take the states in registers) the dq sum computes its own,
  * as retention_chunkwise_bwd does.  INVALID_ARG for a NULL or unaligned
- * fwd_workspace or one that overlaps a gradient; WORKSPACE if it is too small.
+ * fwd_workspace or one that overlaps a gradient or the backward's workspace;
+ * WORKSPACE if it is too small.
  */
 ret_status_t retention_chunkwise_bwd_saved(const void *q, const void *k, const void *v,
                                            const void *d_o, void *dq, void *dk_out, void *dv_out,

@@ -432,6 +432,9 @@ static ret_status_t chunkwise_bwd(const void *q, const void *k, const void *v, c
                 fwd_ws_bytes);
   if (!workspace || workspace_bytes < p.total)
     return fail(RET_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace_bytes);
+  // the backward's own passes write their workspace before the dq sum reads the forward's states
+  if (fwd_ws && overlap(fwd_ws, fwd_plan.seg_bytes, workspace, p.total))
+    return fail(RET_ERR_INVALID_ARG, "the forward workspace overlaps the backward's workspace");
   const size_t R = (size_t)B * H * L;
   const size_t nqk = R * dk * esize(in_dtype), nv = R * dv * esize(in_dtype);
   const size_t oqk = R * dk * esize(out_dtype), ov = R * dv * esize(out_dtype);

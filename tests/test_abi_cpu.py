@@ -189,6 +189,8 @@ def test_backward_with_forward_states_rejects():
     assert call(fwb=fwd_need // 2) == WORKSPACE
     assert b"forward workspace" in L.retention_last_error()
     assert call(dq=FW) == INVALID  # a gradient overlapping the forward's states
+    assert call(fw=WS) == INVALID  # the forward's states inside the backward's workspace
+    assert b"overlaps the backward" in L.retention_last_error()
 
 
 def test_block_rejects():
