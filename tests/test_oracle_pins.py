@@ -19,7 +19,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import TINY, multiscale_gamma, rotation_theta
+from workloads import CHUNKWISE_32K, PARALLEL_2K, TINY, multiscale_gamma, rotation_theta
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -316,3 +316,36 @@ def test_matmul_and_swish_library():
     z = _rand(100, 123) * 4
     assert _rel(oracle.swish(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy()) < 1e-14
     assert oracle.swish(np.zeros(3)).tolist() == [0.0, 0.0, 0.0]
+
+
+def test_parallel_and_recurrent_agree_at_the_parallel_workload():
+    """The parallel workload's reference is the literal double sum; the recurrent
+    form (an independent algorithm) must give the same outputs on four (b, h)
+    slices of its seeded inputs at full length ("Retentive Network" paper summary,
+    Sec. 2.1 (1) and (2))."""
+    wl = PARALLEL_2K
+    q, k, v = wl.qkv()
+    g, th = wl.gamma(), wl.theta()
+    pick = [(0, 0), (3, 2), (5, 5), (7, 7)]
+    sel = lambda t: torch.stack([t[b, h] for b, h in pick])[None]
+    gs = [float(g[h]) for _, h in pick]
+    par = oracle.parallel(sel(q), sel(k), sel(v), gs, th)
+    rec, _ = oracle.recurrent(sel(q), sel(k), sel(v), gs, th)
+    err = np.abs(par - rec).max() / np.abs(par).max()
+    assert err < 1e-11, err
+
+
+def test_recurrent_and_parallel_agree_at_the_chunkwise_workload():
+    """The long-context workload's reference is the recurrent form; the literal
+    double sum must agree with it on the first 4096 tokens of the fastest- and
+    slowest-decaying heads of its seeded inputs (Sec. 2.1 (1) and (2))."""
+    wl = CHUNKWISE_32K
+    q, k, v = wl.qkv()
+    g, th = wl.gamma(), wl.theta()
+    hs, n = [0, wl.H - 1], 4096
+    sel = lambda t: t[:, hs, :n].contiguous()
+    gs = [float(g[h]) for h in hs]
+    par = oracle.parallel(sel(q), sel(k), sel(v), gs, th)
+    rec, _ = oracle.recurrent(sel(q), sel(k), sel(v), gs, th)
+    err = np.abs(par - rec).max() / np.abs(par).max()
+    assert err < 1e-11, err
