@@ -840,6 +840,8 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------- query-block kernel
+constexpr int LPT_G = 4;  // (bh, chunk) units per longest-first task group
+
 // One task = (b, h, chunk c, 64-query block qb).  PAR: the parallel form (one
 // chunk spanning the sequence, no cross term).  Otherwise the chunkwise output
 // with the state entering chunk c, S_c, stored bf16 as S_c^T[dv][dk] in SinT
@@ -854,7 +856,6 @@ __device__ __forceinline__ void lds_barrier() {
 // rotate_keys_kernel), or straight from k when there is no rotation (kt null) --
 // and go to LDS by DMA, no register pass: the next block's DMA is issued once
 // the scores are done with the current one and lands during the P.V products.
-constexpr int LPT_G = 4;  // (bh, chunk) units per longest-first task group
 template <int DK, int DV, bool PAR, bool SPLIT, bool KPRE = false>
 __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, const uint16_t *SinT,
                                                     const uint16_t *kt = nullptr) {
@@ -882,9 +883,9 @@ __global__ __launch_bounds__(NT) void qblock_kernel(RetArgs a, TaskGeom geo, con
   // inside a group the query blocks run from the last (the most key blocks to
   // visit) to the first, across the group's units.  Each XCD takes a contiguous
   // range of tasks (xcd_task), so it starts on the long tasks of its groups and
-  // fills its tail with short ones, while the few units in flight at a time keep
-  // their K and V in that XCD's L2.  (Units one after another, longest first
-  // within each: parallel workload 383 -> 353 us, MSR layer 1245 -> 1207 us.)
+  // fills its tail with short ones.  (Units one after another, longest first
+  // within each: parallel workload 383 -> 353 us, MSR layer 1245 -> 1207 us; the
+  // four units in flight re-read more K and V past the L2, which costs less.)
   int qb = 0, c = 0, bh = task;  // sel 1: one task per (b, h), its first query block
   if (geo.sel != 1) {
     const int nunits = geo.ntasks / geo.nqb, grp = task / (geo.nqb * LPT_G);
